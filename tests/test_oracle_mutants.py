@@ -1,0 +1,50 @@
+"""Plant plausible mistakes in copies of the CPU oracle and check that the pins
+catch every one.  Runs on the CPU only: each mutant is a g++ build of the
+oracle source with one textual change, loaded from a temporary directory.
+"""
+import pytest
+
+from oracle import lqref
+from tests.test_oracle_pins import ALL_PINS
+
+MUTANTS = {
+    # nibble order (2j, 2j+1) instead of (j, j+16)
+    "nibble_order": ("out[j] = static_cast<double>(lo - 8) * d;\n        out[j + 16] = static_cast<double>(hi - 8) * d;",
+                     "out[2 * j] = static_cast<double>(lo - 8) * d;\n        out[2 * j + 1] = static_cast<double>(hi - 8) * d;"),
+    # the -8 offset dropped from the low nibble
+    "drop_offset": ("out[j] = static_cast<double>(lo - 8) * d;", "out[j] = static_cast<double>(lo) * d;"),
+    # fp16 exponent bias off by one
+    "half_bias": ("std::ldexp(static_cast<double>(1024 + m), e - 25)", "std::ldexp(static_cast<double>(1024 + m), e - 24)"),
+    # fp16 subnormal scale wrong
+    "half_subnormal": ("std::ldexp(static_cast<double>(m), -24)", "std::ldexp(static_cast<double>(m), -25)"),
+    # Q8_0 codes read as unsigned
+    "q8_unsigned": ("const int c = static_cast<int8_t>(b[2 + j]);", "const int c = b[2 + j];"),
+    # scale bytes read big-endian
+    "scale_endianness": ("const double d = half_to_double(static_cast<uint16_t>(b[0] | (b[1] << 8)));\n    for (int j = 0; j < 16; ++j)",
+                         "const double d = half_to_double(static_cast<uint16_t>((b[0] << 8) | b[1]));\n    for (int j = 0; j < 16; ++j)"),
+    # int8 block-64 scale index using 32-wide blocks
+    "i8_scale_index": ("static_cast<double>(s[k / 64])", "static_cast<double>(s[k / 32 % (K / 64)])"),
+    # S without the absolute value
+    "abs_dropped": ("abs_acc += std::fabs(p);\n        }\n        y[i] = acc;", "abs_acc += p;\n        }\n        y[i] = acc;"),
+    # GEMM reads X transposed
+    "gemm_transposed_x": ("x_at(X, xdt, ms[a] * K + k)", "x_at(X, xdt, k * M + ms[a])"),
+    # fp16 encoder rounds ties up instead of to even
+    "ties_up": ("return (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    # GEMM ignores the fp16 tile rounding flag
+    "gemm_no_f16_round": ("if (round_w_f16)", "if (false && round_w_f16)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = lqref.source_text()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant = lqref.build_variant(src.replace(old, new), str(tmp_path))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
