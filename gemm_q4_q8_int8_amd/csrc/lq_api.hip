@@ -1,0 +1,290 @@
+// liblq C ABI: argument validation, launch configuration and error reporting.
+// Every check runs before the first HIP call of an entry point, so a rejected
+// call leaves device and stream untouched.
+#include "../../include/lq.h"
+#include "lq_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lq_status fail(lq_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+lq_status hip_fail(hipError_t e, const char* what) {
+    return fail(LQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool fmt_ok(int32_t f) { return f == LQ_Q4_0 || f == LQ_Q8_0 || f == LQ_I8B64; }
+int32_t block_of(int32_t f) { return f == LQ_I8B64 ? 64 : (fmt_ok(f) ? 32 : 0); }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+constexpr int64_t kMaxDim = 2147483647;
+
+lq_status check_fmt_shape(int32_t fmt, int64_t N, int64_t K) {
+    if (!fmt_ok(fmt)) return fail(LQ_ERR_FMT, "unknown weight format %d", fmt);
+    if (N < 1 || N > kMaxDim) return fail(LQ_ERR_SHAPE, "N=%lld out of range [1, 2^31-1]", (long long)N);
+    if (K < 1 || K > kMaxDim) return fail(LQ_ERR_SHAPE, "K=%lld out of range [1, 2^31-1]", (long long)K);
+    if (K % block_of(fmt) != 0)
+        return fail(LQ_ERR_SHAPE, "K=%lld is not a multiple of the block size %d", (long long)K, block_of(fmt));
+    if (N * (K / 32) > (int64_t(1) << 40)) return fail(LQ_ERR_SHAPE, "matrix too large");
+    return LQ_OK;
+}
+
+lq_status check_ptr(const void* p, uintptr_t align, const char* name) {
+    if (!p) return fail(LQ_ERR_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(LQ_ERR_ALIGN, "%s is not %u-byte aligned", name, unsigned(align));
+    return LQ_OK;
+}
+
+lq_status check_xdt(int32_t xdt) {
+    if (xdt != LQ_F32 && xdt != LQ_F16) return fail(LQ_ERR_DTYPE, "unknown activation dtype %d", xdt);
+    return LQ_OK;
+}
+
+#define LQ_TRY(expr)                    \
+    do {                                \
+        const lq_status st__ = (expr);  \
+        if (st__ != LQ_OK) return st__; \
+    } while (0)
+
+// Per-device compute-unit counts, filled on first use of a device.
+std::mutex g_dev_mu;
+int g_cus[64] = {0};
+
+lq_status device_cus(int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(LQ_ERR_HIP, "device index %d unsupported", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_cus[dev] == 0) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        g_cus[dev] = n > 0 ? n : 1;
+    }
+    *cus = g_cus[dev];
+    return LQ_OK;
+}
+
+lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
+    lq_status st = check_fmt_shape(d.fmt, d.N, d.K);
+    if (st != LQ_OK) return st;
+    st = check_xdt(d.xdt);
+    if (st != LQ_OK) return st;
+    if (!d.W || !d.x || !d.y) return fail(LQ_ERR_ARG, "descriptor %d: W, x or y is NULL", idx);
+    if (!aligned(d.W, 16) || !aligned(d.x, 16))
+        return fail(LQ_ERR_ALIGN, "descriptor %d: W and x must be 16-byte aligned", idx);
+    if (!aligned(d.y, 4)) return fail(LQ_ERR_ALIGN, "descriptor %d: y must be 4-byte aligned", idx);
+    return LQ_OK;
+}
+
+// Fill one descriptor of a grouped GEMV launch.
+lq::GemvDesc make_desc(const lq_gemv_desc& d, int rows_per_iter) {
+    lq::GemvDesc g;
+    g.codes = static_cast<const uint8_t*>(d.W);
+    g.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(d.fmt, d.N, d.K));
+    g.x = d.x;
+    g.y = d.y;
+    g.N = int32_t(d.N);
+    g.nu = int32_t(d.K / 32);
+    g.xdt = d.xdt;
+    g.iters = int32_t((d.N + rows_per_iter - 1) / rows_per_iter);
+    return g;
+}
+
+lq_status launch_group(int fmt, const lq::GemvConfig& cfg, const std::vector<const lq_gemv_desc*>& g,
+                       int cus, hipStream_t stream) {
+    for (size_t base = 0; base < g.size(); base += lq::kMaxBatch) {
+        lq::GemvBatchArgs a = {};
+        const size_t cnt = std::min(g.size() - base, size_t(lq::kMaxBatch));
+        a.count = int32_t(cnt);
+        a.prefix[0] = 0;
+        for (size_t i = 0; i < cnt; ++i) {
+            a.d[i] = make_desc(*g[base + i], cfg.rows_per_iter);
+            a.prefix[i + 1] = a.prefix[i] + a.d[i].iters;
+        }
+        const int total = a.prefix[cnt];
+        // Enough workgroups to fill every CU several times over, each walking
+        // an equal share of the row iterations.
+        const int cap = cus * 8;
+        const int per = (total + cap - 1) / cap;
+        const int grid = (total + per - 1) / per;
+        const hipError_t e = lq::launch_gemv(fmt, cfg, a, grid, stream);
+        if (e != hipSuccess) return hip_fail(e, "GEMV launch");
+    }
+    return LQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lq_abi_version(void) { return LQ_ABI_VERSION; }
+
+lq_status lq_init(void) {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (n < 1) return fail(LQ_ERR_HIP, "no HIP device present");
+    int cus = 0;
+    return device_cus(&cus);
+}
+
+int32_t lq_block_elems(int32_t fmt) { return block_of(fmt); }
+
+size_t lq_packed_bytes(int32_t fmt, int64_t N, int64_t K) {
+    if (check_fmt_shape(fmt, N, K) != LQ_OK) return 0;
+    return lq::align256(lq::code_plane_bytes(fmt, N, K)) + lq::scale_plane_bytes(fmt, N, K);
+}
+
+size_t lq_scale_offset(int32_t fmt, int64_t N, int64_t K) {
+    if (check_fmt_shape(fmt, N, K) != LQ_OK) return 0;
+    return lq::align256(lq::code_plane_bytes(fmt, N, K));
+}
+
+size_t lq_gguf_bytes(int32_t fmt, int64_t N, int64_t K) {
+    if (fmt == LQ_I8B64 || check_fmt_shape(fmt, N, K) != LQ_OK) return 0;
+    return size_t(N) * size_t(K / 32) * (fmt == LQ_Q4_0 ? 18 : 34);
+}
+
+lq_status lq_repack_gguf(int32_t fmt, const void* src, void* dst, int64_t N, int64_t K, void* stream) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    if (fmt == LQ_I8B64) return fail(LQ_ERR_FMT, "LQ_I8B64 has no GGUF form; use lq_pack_planes");
+    LQ_TRY(check_ptr(src, 2, "src"));
+    LQ_TRY(check_ptr(dst, 16, "dst"));
+    const hipError_t e = lq::launch_repack_gguf(fmt, src, dst, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "repack launch");
+}
+
+lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales, void* dst, int64_t N,
+                         int64_t K, void* stream) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    LQ_TRY(check_ptr(codes, 16, "codes"));
+    LQ_TRY(check_ptr(scales, 4, "scales"));
+    LQ_TRY(check_ptr(dst, 16, "dst"));
+    const size_t cb = lq::code_plane_bytes(fmt, N, K);
+    const size_t sb = lq::scale_plane_bytes(fmt, N, K);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(dst, codes, cb, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "code plane copy");
+    e = hipMemcpyAsync(static_cast<uint8_t*>(dst) + lq::align256(cb), scales, sb, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "scale plane copy");
+    return LQ_OK;
+}
+
+static lq_status dequant_common(int32_t fmt, const void* W, void* out, int64_t N, int64_t K,
+                                void* stream, bool f16) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    LQ_TRY(check_ptr(W, 16, "W"));
+    LQ_TRY(check_ptr(out, 16, "out"));
+    const hipError_t e = lq::launch_dequant(fmt, f16, W, out, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "dequant launch");
+}
+
+lq_status lq_dequant_f32(int32_t fmt, const void* W, float* out, int64_t N, int64_t K, void* stream) {
+    return dequant_common(fmt, W, out, N, K, stream, false);
+}
+
+lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out, int64_t N, int64_t K, void* stream) {
+    return dequant_common(fmt, W, out, N, K, stream, true);
+}
+
+lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream) {
+    if (!descs) return fail(LQ_ERR_ARG, "descs is NULL");
+    if (count < 1) return fail(LQ_ERR_ARG, "count=%d must be >= 1", count);
+    for (int32_t i = 0; i < count; ++i) LQ_TRY(check_gemv_desc(descs[i], i));
+    int cus = 0;
+    LQ_TRY(device_cus(&cus));
+    // Group descriptors that share a kernel (format and team shape), keeping
+    // their order, and launch each group in chunks of kMaxBatch.
+    std::vector<bool> done(size_t(count), false);
+    for (int32_t i = 0; i < count; ++i) {
+        if (done[i]) continue;
+        const lq::GemvConfig cfg = lq::gemv_config(int(descs[i].K / 32));
+        std::vector<const lq_gemv_desc*> group;
+        for (int32_t j = i; j < count; ++j) {
+            if (done[j] || descs[j].fmt != descs[i].fmt) continue;
+            const lq::GemvConfig cj = lq::gemv_config(int(descs[j].K / 32));
+            if (cj.tp != cfg.tp || cj.upl != cfg.upl) continue;
+            group.push_back(&descs[j]);
+            done[j] = true;
+        }
+        LQ_TRY(launch_group(descs[i].fmt, cfg, group, cus, static_cast<hipStream_t>(stream)));
+    }
+    return LQ_OK;
+}
+
+lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt, float* y, int64_t N,
+                  int64_t K, void* stream) {
+    lq_gemv_desc d;
+    d.fmt = fmt;
+    d.xdt = xdt;
+    d.W = W;
+    d.x = x;
+    d.y = y;
+    d.N = N;
+    d.K = K;
+    return lq_gemv_batch(&d, 1, stream);
+}
+
+size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+    if (check_fmt_shape(fmt, N, K) != LQ_OK || M < 1) return 0;
+    return lq::gemm_workspace_bytes(M, N, K);
+}
+
+lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
+                  int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    LQ_TRY(check_xdt(xdt));
+    if (M < 1 || M > kMaxDim) return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, 2^31-1]", (long long)M);
+    if (fmt != LQ_Q4_0 || xdt != LQ_F16)
+        return fail(LQ_ERR_UNSUPPORTED, "lq_gemm implements LQ_Q4_0 weights with LQ_F16 activations");
+    LQ_TRY(check_ptr(W, 16, "W"));
+    LQ_TRY(check_ptr(X, 16, "X"));
+    LQ_TRY(check_ptr(Y, 4, "Y"));
+    const size_t need = lq::gemm_workspace_bytes(M, N, K);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, ws_bytes);
+    if (ws && !aligned(ws, 16)) return fail(LQ_ERR_ALIGN, "ws is not 16-byte aligned");
+    int cus = 0;
+    LQ_TRY(device_cus(&cus));
+    const hipError_t e = lq::launch_gemm_q4_0(W, X, Y, M, N, K, ws, ws_bytes, cus,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
+}
+
+lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
+                    int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+    if (M == 1) return lq_gemv(fmt, W, X, xdt, Y, N, K, stream);
+    return lq_gemm(fmt, W, X, xdt, Y, M, N, K, ws, ws_bytes, stream);
+}
+
+const char* lq_status_str(int32_t status) {
+    switch (status) {
+        case LQ_OK: return "LQ_OK";
+        case LQ_ERR_ARG: return "LQ_ERR_ARG";
+        case LQ_ERR_SHAPE: return "LQ_ERR_SHAPE";
+        case LQ_ERR_ALIGN: return "LQ_ERR_ALIGN";
+        case LQ_ERR_FMT: return "LQ_ERR_FMT";
+        case LQ_ERR_DTYPE: return "LQ_ERR_DTYPE";
+        case LQ_ERR_UNSUPPORTED: return "LQ_ERR_UNSUPPORTED";
+        case LQ_ERR_WORKSPACE: return "LQ_ERR_WORKSPACE";
+        case LQ_ERR_HIP: return "LQ_ERR_HIP";
+        default: return "LQ_ERR_UNKNOWN";
+    }
+}
+
+const char* lq_last_error(void) { return g_err; }
+
+}  // extern "C"

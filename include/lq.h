@@ -1,0 +1,195 @@
+/*
+ * lq.h — C ABI of liblq: block-quantized weight x activation products on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A weight matrix W has N rows and K columns and is stored in
+ * blocks that run along K.  The library computes y = W x for one token (a
+ * dequantizing matrix-vector product, the decode step) and Y = X W^T for a
+ * chunk of M tokens (the prefill matrix product).  "Decode is memory-bandwidth
+ * bound: every generated token streams all dense weights once", while prefill
+ * is compute-bound ("oxinfer" page, "Performance"); prefill GPU kernels
+ * dequantize weights into on-chip memory and run a dense tile ("oxinfer" page,
+ * "Platforms and accelerators" and "Browser (WebGPU)").
+ *
+ * Weight formats (enum lq_fmt):
+ *   LQ_Q4_0   GGUF Q4_0 ("lean" page, model table; "oxinfer" page, "How it
+ *             works": two nibbles per byte, f16 scale).  32 weights per block,
+ *             one fp16 scale d, 4-bit codes q; w = (q - 8) * d.  Within a
+ *             block's 16 code bytes, byte j holds element j in its low nibble
+ *             and element j + 16 in its high nibble (the GGUF order).
+ *   LQ_Q8_0   GGUF Q8_0 ("lean" page, Q8_0 parity fixtures).  32 int8 codes c
+ *             and one fp16 scale d per block; w = c * d.
+ *   LQ_I8B64  symmetric int8 with block size 64 ("wgpu-llm" page, "INT8
+ *             mode", --block-size 64).  int8 codes c, one fp32 scale s per 64
+ *             consecutive codes of a row; w = c * s (no zero point).
+ *
+ * Packed layout (what every W argument points to).  Like the split layout in
+ * which the "oxinfer" page stores quantized matrices ("Pre-quantized
+ * checkpoints": codes and scales as separate tensors, in the kernels'
+ * in-memory layout), a packed matrix is a code plane followed by a scale
+ * plane.  With nb = K / block blocks per row and b = n * nb + (block index):
+ *   LQ_Q4_0   codes: 16 bytes per block at offset 16 * b, GGUF byte order;
+ *             scales: fp16 at offset lq_scale_offset() + 2 * b.
+ *   LQ_Q8_0   codes: 32 int8 per block at offset 32 * b;
+ *             scales: fp16 at offset lq_scale_offset() + 2 * b.
+ *   LQ_I8B64  codes: int8, row-major N x K, at offset n * K + k;
+ *             scales: fp32 at offset lq_scale_offset() + 4 * (n * K / 64 + k / 64).
+ *   lq_scale_offset() is the code-plane size rounded up to 256 bytes.  The
+ *   weight bytes equal those of the GGUF form (18 or 34 bytes per 32
+ *   weights; 68 bytes per 64 for LQ_I8B64) plus at most 255 bytes of padding.
+ *
+ * Conventions for every call.
+ *   - Pointers named W, x, X, y, Y, out, dst, src, codes, scales, ws are
+ *     DEVICE pointers (memory the caller allocated on the current HIP device);
+ *     `descs` of lq_gemv_batch is a HOST pointer.  The caller owns every
+ *     buffer; the library keeps no pointer after a call returns and allocates
+ *     no device memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Calls only enqueue work (no implicit synchronisation); results are
+ *     ready when the stream reaches that point.
+ *   - Sizes are int64_t: N, K, M >= 1; N <= 2^31 - 1, M <= 2^31 - 1.  K must be
+ *     a multiple of the format's block (32, 32, 64).
+ *   - Alignment: W, x, X, dst, out and codes must be 16-byte aligned; y, Y
+ *     and scales 4-byte aligned; src (GGUF bytes) 2-byte aligned.
+ *   - Activations: x / X are fp32 (LQ_F32) or fp16 (LQ_F16), contiguous; X is
+ *     M x K row-major (token-major).  Outputs y / Y are always fp32.
+ *   - Output buffers must not overlap inputs (undefined behaviour, unchecked).
+ *   - Errors: every call returns an lq_status.  All argument checks happen
+ *     before any HIP call, so a rejected call touches no device state.  On a
+ *     failure lq_last_error() returns a message for the calling thread.
+ *     Nothing aborts, prints or throws across the ABI.
+ *   - Thread safety: calls may come from several host threads; calls that
+ *     write the same buffers must be ordered by the caller.
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LQ_ABI_VERSION 1
+
+typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2 } lq_fmt;
+typedef enum lq_dtype { LQ_F32 = 0, LQ_F16 = 1 } lq_dtype;
+
+typedef enum lq_status {
+    LQ_OK = 0,
+    LQ_ERR_ARG = 1,          /* null pointer, bad count, bad enum-like value */
+    LQ_ERR_SHAPE = 2,        /* N, K or M out of range, K not a block multiple */
+    LQ_ERR_ALIGN = 3,        /* a pointer misses its required alignment */
+    LQ_ERR_FMT = 4,          /* unknown format, or format not valid for the call */
+    LQ_ERR_DTYPE = 5,        /* unknown activation dtype */
+    LQ_ERR_UNSUPPORTED = 6,  /* valid combination this version does not implement */
+    LQ_ERR_WORKSPACE = 7,    /* workspace missing or smaller than required */
+    LQ_ERR_HIP = 8           /* no HIP device, or a HIP runtime call failed */
+} lq_status;
+
+/* Returns LQ_ABI_VERSION. */
+int32_t lq_abi_version(void);
+
+/* Checks that a HIP device is present and caches its properties.  Returns
+ * LQ_ERR_HIP (with a message) when there is none.  Other calls initialise on
+ * first use; calling this first is optional. */
+lq_status lq_init(void);
+
+/* Weights per block of `fmt` (32, 32, 64); 0 for an unknown format. */
+int32_t lq_block_elems(int32_t fmt);
+
+/* Bytes of the packed layout above for an N x K matrix; 0 if fmt, N or K is
+ * invalid. */
+size_t lq_packed_bytes(int32_t fmt, int64_t N, int64_t K);
+
+/* Offset of the scale plane inside the packed layout; 0 if invalid. */
+size_t lq_scale_offset(int32_t fmt, int64_t N, int64_t K);
+
+/* Bytes of the GGUF array-of-blocks form (18 or 34 bytes per block); 0 for
+ * LQ_I8B64 (no GGUF form) or invalid arguments. */
+size_t lq_gguf_bytes(int32_t fmt, int64_t N, int64_t K);
+
+/* GGUF array-of-blocks -> packed layout (a byte permutation, no arithmetic).
+ * src: N*K/32 GGUF blocks, each the fp16 scale (little-endian) followed by
+ * the codes, as a GGUF reader holds them ("lean" page: the engine reads
+ * quantized GGUF files).  dst: lq_packed_bytes() bytes.  LQ_I8B64 returns
+ * LQ_ERR_FMT: it has no GGUF form (use lq_pack_planes). */
+lq_status lq_repack_gguf(int32_t fmt, const void* src, void* dst,
+                         int64_t N, int64_t K, void* stream);
+
+/* Separate code and scale planes -> packed layout (two device copies).
+ * codes: the code plane exactly as described above (N*nb*16 bytes for Q4_0,
+ * N*K bytes for Q8_0 and LQ_I8B64); scales: N*nb fp16 (Q4_0, Q8_0) or
+ * N*K/64 fp32 (LQ_I8B64).  This is the "oxinfer" page's split form
+ * ("Pre-quantized checkpoints": X.q4 + X.q4s, X.q8 + X.q8s). */
+lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales,
+                         void* dst, int64_t N, int64_t K, void* stream);
+
+/* Unpacked weights: out[n*K + k] = RN_fp32(w[n,k]).  Exact for Q4_0 and Q8_0
+ * (the product of a small integer and an fp16 scale fits fp32); one IEEE
+ * rounding of c * s for LQ_I8B64.  out: N*K fp32, 16-byte aligned. */
+lq_status lq_dequant_f32(int32_t fmt, const void* W, float* out,
+                         int64_t N, int64_t K, void* stream);
+
+/* Unpacked weights rounded once to fp16 (bit patterns): out[n*K + k] =
+ * RN_fp16(w[n,k]), round to nearest even, subnormals kept, overflow to inf.
+ * This is the tile contract of lq_gemm.  out: N*K uint16, 16-byte aligned. */
+lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out,
+                         int64_t N, int64_t K, void* stream);
+
+/* Decode GEMV: y[n] = sum_k w[n,k] * x[k] for n < N, accumulated in fp32 with
+ * the weights decoded exactly.  W: packed N x K; x: K values of dtype xdt;
+ * y: N fp32.  Accuracy: |y - y_exact| <= 1e-4 * sum_k |w x| + 1e-6 per row. */
+lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt,
+                  float* y, int64_t N, int64_t K, void* stream);
+
+/* One independent GEMV for lq_gemv_batch (fields as in lq_gemv). */
+typedef struct lq_gemv_desc {
+    int32_t fmt;
+    int32_t xdt;
+    const void* W;
+    const void* x;
+    float* y;
+    int64_t N;
+    int64_t K;
+} lq_gemv_desc;
+
+/* Grouped launch of `count` independent GEMVs (for example every projection of
+ * a decoder layer), so that small matrices share launches.  descs: HOST array
+ * of `count` descriptors (count >= 1), read during the call only.  Every
+ * descriptor is validated before anything is enqueued. */
+lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
+
+/* Workspace bytes lq_gemm needs for these arguments (0 means none). */
+size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
+
+/* Prefill GEMM: Y[m,n] = sum_k RN_fp16(w[n,k]) * X[m,k], products and sums in
+ * fp32 on the matrix cores.  W: packed N x K; X: M x K fp16 row-major;
+ * Y: M x N fp32 row-major.  ws / ws_bytes: workspace of at least
+ * lq_gemm_workspace_bytes() bytes (may be NULL when that is 0).  Accuracy:
+ * |Y - Y_exact| <= 2e-3 * sum_k |w x| + 1e-5 per element.  This version
+ * implements fmt LQ_Q4_0 with xdt LQ_F16; other combinations return
+ * LQ_ERR_UNSUPPORTED. */
+lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt,
+                  float* Y, int64_t M, int64_t N, int64_t K,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Route by token count, after the "oxinfer" page's rule that GPU matmul
+ * kernels take only prompt-sized work ("Platforms and accelerators": t >= 16
+ * tokens): M == 1 runs lq_gemv on X (fp32 or fp16); M >= 2 runs lq_gemm.
+ * Arguments as in lq_gemm. */
+lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt,
+                    float* Y, int64_t M, int64_t N, int64_t K,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Name of a status code ("LQ_OK", ...). */
+const char* lq_status_str(int32_t status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* lq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LQ_H */

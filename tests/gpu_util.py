@@ -1,0 +1,57 @@
+"""Shared helpers of the GPU parity tests: upload, run through the C ABI,
+compare with the oracle under the stated tolerances."""
+import numpy as np
+import torch
+
+import gemm_q4_q8_int8_amd as lq
+from gemm_q4_q8_int8_amd.device import to_device, upload_gguf, upload_planes
+
+FMT = {"q4_0": lq.LQ_Q4_0, "q8_0": lq.LQ_Q8_0, "i8b64": lq.LQ_I8B64}
+GUARD = 1024            # canary floats after every output buffer
+SENTINEL = -12345.5
+
+GEMV_REL, GEMV_ABS = 1e-4, 1e-6     # |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per row
+GEMM_REL, GEMM_ABS = 2e-3, 1e-5     # |Y - Y_ref| <= 2e-3 * sum|w x| + 1e-5 per element
+
+
+def upload(fmt: str, w, scales, N, K):
+    if fmt == "i8b64":
+        return upload_planes(FMT[fmt], w, scales, N, K)
+    return upload_gguf(FMT[fmt], w, N, K)
+
+
+def guarded(n, dtype=torch.float32):
+    buf = torch.full((n + GUARD,), SENTINEL, dtype=dtype, device="cuda")
+    return buf
+
+
+def check_guard(buf, n):
+    tail = buf[n:].cpu().numpy()
+    assert np.all(tail == SENTINEL), "write past the end of the output buffer"
+
+
+def gemv(fmt: str, Wd, x: np.ndarray, N, K):
+    xd = to_device(x)
+    y = guarded(N)
+    lq.lq_gemv(FMT[fmt], Wd, xd, y, N, K)
+    torch.cuda.synchronize()
+    check_guard(y, N)
+    return y[:N].cpu().numpy()
+
+
+def gemm(Wd, X: np.ndarray, M, N, K):
+    Xd = to_device(X)
+    Y = guarded(M * N)
+    ws_bytes = lq.lq_gemm_workspace_bytes(lq.LQ_Q4_0, M, N, K)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    lq.lq_gemm(lq.LQ_Q4_0, Wd, Xd, Y, M, N, K, ws=ws, ws_bytes=ws_bytes)
+    torch.cuda.synchronize()
+    check_guard(Y, M * N)
+    return Y[:M * N].cpu().numpy().reshape(M, N)
+
+
+def ratio(y, yref, S, rel, abs_):
+    """max over elements of |y - y_ref| / (rel * S + abs_); parity holds when <= 1."""
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), "non-finite output"
+    return float(np.max(np.abs(y - yref) / (rel * S + abs_))) if y.size else 0.0

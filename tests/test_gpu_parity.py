@@ -1,0 +1,370 @@
+"""GPU parity of liblq against the CPU oracle (needs an MI355X).
+
+Every case prints its name before it touches the GPU.  Inputs come from the
+seeded generator; expected values come only from the oracle or from the
+hand-built blocks.  Bars: unpacked weights bit-exact; GEMV per row
+|y - y_ref| <= 1e-4 * sum|w x| + 1e-6; GEMM per element
+|Y - Y_ref| <= 2e-3 * sum|w x| + 1e-5.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_q4_q8_int8_amd as lq
+import lqgen
+from gemm_q4_q8_int8_amd.device import to_device
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+ORACLE_FMT = {"q4_0": 0, "q8_0": 1, "i8b64": 2}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    lq.load()
+    lq.lq_init()
+    yield
+
+
+def make(fmt, seed, N, K, c=None):
+    if fmt == "q4_0":
+        return lqgen.q4_0_aos(seed, N, K, c or 0.02), None
+    if fmt == "q8_0":
+        return lqgen.q8_0_aos(seed, N, K, c or 0.005), None
+    return lqgen.i8b64_planes(seed, N, K, c or 0.003)
+
+
+def set_scales(fmt, w, scales, N, K, values):
+    """Overwrite the first scales of a generated matrix with special values."""
+    if fmt == "i8b64":
+        s = scales.copy()
+        s[:len(values)] = np.array(values, np.float32)
+        return w, s
+    bb = 18 if fmt == "q4_0" else 34
+    blk = w.reshape(-1, bb).copy()
+    for i, v in enumerate(values):
+        blk[i, 0:2] = np.array([v], np.float64).astype(np.float16).view(np.uint8)
+    return blk.reshape(-1), None
+
+
+def ref_dequant(o, fmt, w, scales, N, K):
+    return o.dequant_f32(ORACLE_FMT[fmt], w, scales, N, K), o.dequant_f16(ORACLE_FMT[fmt], w, scales, N, K)
+
+
+# ------------------------------------------------------------- dequant ----
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+def test_dequant_bitwise(oracle, fmt):
+    N, K = 37, 448 if fmt != "i8b64" else 448
+    say("dequant", fmt, N, K)
+    w, s = make(fmt, 101, N, K)
+    specials = [2.0 ** -24, -2.0 ** -24, 3 * 2.0 ** -20, -0.0, 0.0, -1.5, 65504.0, np.inf, -np.inf, np.nan,
+                6.1e-5, 1e-7]
+    w, s = set_scales(fmt, w, s, N, K, specials)
+    Wd = gu.upload(fmt, w, s, N, K)
+    out32 = torch.empty(N * K, dtype=torch.float32, device="cuda")
+    out16 = torch.empty(N * K, dtype=torch.uint16, device="cuda")
+    lq.lq_dequant_f32(gu.FMT[fmt], Wd, out32, N, K)
+    lq.lq_dequant_f16(gu.FMT[fmt], Wd, out16, N, K)
+    torch.cuda.synchronize()
+    g32 = out32.cpu().numpy().reshape(N, K)
+    g16 = out16.cpu().numpy().reshape(N, K)
+    r32, r16 = ref_dequant(oracle, fmt, w, s, N, K)
+    nan = np.isnan(r32)
+    assert np.array_equal(np.isnan(g32), nan)
+    assert np.array_equal(g32.view(np.uint32)[~nan], r32.view(np.uint32)[~nan])
+    n16 = np.isnan(r16.view(np.float16))
+    assert np.array_equal(np.isnan(g16.view(np.float16)), n16)
+    assert np.array_equal(g16[~n16], r16[~n16])
+
+
+def test_dequant_golden_blocks(oracle):
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "blocks.json")))
+    for blk in gold["blocks"]:
+        say("golden block", blk["id"])
+        raw = np.frombuffer(bytes.fromhex(blk["hex"]), np.uint8).copy()
+        Wd = gu.upload(blk["fmt"], raw, None, 1, 32)
+        out32 = torch.empty(32, dtype=torch.float32, device="cuda")
+        out16 = torch.empty(32, dtype=torch.uint16, device="cuda")
+        lq.lq_dequant_f32(gu.FMT[blk["fmt"]], Wd, out32, 1, 32)
+        lq.lq_dequant_f16(gu.FMT[blk["fmt"]], Wd, out16, 1, 32)
+        torch.cuda.synchronize()
+        want = np.array([float(v) for v in blk["expected"]]).astype(np.float32)
+        assert np.array_equal(out32.cpu().numpy().view(np.uint32), want.view(np.uint32)), blk["id"]
+        want16 = np.array([float(v) for v in blk.get("f16", blk["expected"])]).astype(np.float16)
+        assert np.array_equal(out16.cpu().numpy(), want16.view(np.uint16)), blk["id"]
+        y = gu.gemv(blk["fmt"], Wd, np.ones(32, np.float32), 1, 32)
+        if np.isfinite(float(blk["sum"])) and abs(float(blk["sum"])) < 1e6:
+            assert y[0] == np.float32(float(blk["sum"])), blk["id"]
+
+
+def test_repack_roundtrip_planes():
+    """GGUF -> packed by lq_repack_gguf equals the plane layout built on the host."""
+    for fmt in ("q4_0", "q8_0"):
+        N, K = 9, 224
+        say("repack layout", fmt)
+        w, _ = make(fmt, 77, N, K)
+        Wd = gu.upload(fmt, w, None, N, K)
+        packed = Wd.cpu().numpy()
+        bb = 18 if fmt == "q4_0" else 34
+        blk = w.reshape(-1, bb)
+        code_plane = blk[:, 2:].reshape(-1)
+        off = lq.lq_scale_offset(gu.FMT[fmt], N, K)
+        assert np.array_equal(packed[:code_plane.size], code_plane)
+        assert np.array_equal(packed[off:off + 2 * blk.shape[0]], blk[:, 0:2].reshape(-1))
+
+
+# ---------------------------------------------------------------- GEMV ----
+
+GEMV_SHAPES = [
+    ("q4_0", 1, 32), ("q4_0", 5, 64), ("q4_0", 67, 96), ("q4_0", 300, 896), ("q4_0", 129, 960),
+    ("q4_0", 33, 2048), ("q4_0", 40, 4864), ("q4_0", 17, 11008), ("q4_0", 9, 25600),
+    ("q8_0", 1, 32), ("q8_0", 70, 512), ("q8_0", 130, 2048), ("q8_0", 31, 5632), ("q8_0", 24, 8192),
+    ("q8_0", 6, 26624),
+    ("i8b64", 1, 64), ("i8b64", 77, 128), ("i8b64", 256, 2048), ("i8b64", 45, 5632),
+    ("i8b64", 12, 8192), ("i8b64", 5, 30720),
+]
+
+
+@pytest.mark.parametrize("fmt,N,K", GEMV_SHAPES)
+@pytest.mark.parametrize("xdt", [np.float32, np.float16], ids=["xf32", "xf16"])
+def test_gemv_parity(oracle, fmt, N, K, xdt):
+    say("gemv", fmt, N, K, np.dtype(xdt).name)
+    w, s = make(fmt, 1000 + N + K, N, K)
+    if N > 3:
+        w, s = set_scales(fmt, w, s, N, K, [2.0 ** -24, -0.75, 0.0, 3e-6])
+    x = lqgen.activations(4242 + K, K, xdt)
+    Wd = gu.upload(fmt, w, s, N, K)
+    y = gu.gemv(fmt, Wd, x, N, K)
+    yr, S = oracle.gemv(ORACLE_FMT[fmt], w, s, x, N, K)
+    r = gu.ratio(y, yr, S, gu.GEMV_REL, gu.GEMV_ABS)
+    assert r <= 1.0, f"tolerance ratio {r}"
+
+
+def test_gemv_batch_mixed(oracle):
+    """More than one launch group and more descriptors than one launch holds."""
+    cases = []
+    for i in range(20):
+        fmt = ["q4_0", "q8_0", "i8b64"][i % 3]
+        K = [64, 896, 2048, 5632][i % 4] if fmt != "i8b64" else [64, 2048, 5632][i % 3]
+        N = 13 + 37 * i
+        xdt = np.float16 if i % 2 else np.float32
+        w, s = make(fmt, 500 + i, N, K)
+        x = lqgen.activations(900 + i, K, xdt)
+        cases.append((fmt, N, K, w, s, x))
+    say("gemv batch of", len(cases))
+    descs, outs = [], []
+    for fmt, N, K, w, s, x in cases:
+        Wd = gu.upload(fmt, w, s, N, K)
+        xd = to_device(x)
+        y = gu.guarded(N)
+        descs.append((gu.FMT[fmt], Wd, xd, y, N, K))
+        outs.append(y)
+    lq.lq_gemv_batch(descs)
+    torch.cuda.synchronize()
+    for (fmt, N, K, w, s, x), y in zip(cases, outs):
+        gu.check_guard(y, N)
+        yr, S = oracle.gemv(ORACLE_FMT[fmt], w, s, x, N, K)
+        assert gu.ratio(y[:N].cpu().numpy(), yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, (fmt, N, K)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+def test_gemv_invariants(oracle, fmt):
+    N, K = 96, 2048 if fmt != "q4_0" else 896
+    say("gemv invariants", fmt, N, K)
+    w, s = make(fmt, 31337, N, K)
+    x = lqgen.activations(7, K, np.float32)
+    Wd = gu.upload(fmt, w, s, N, K)
+    y1 = gu.gemv(fmt, Wd, x, N, K)
+    y2 = gu.gemv(fmt, Wd, x, N, K)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+    # every scale doubled -> y doubles bit for bit
+    if fmt == "i8b64":
+        w2, s2 = w, s * np.float32(2)
+    else:
+        bb = 18 if fmt == "q4_0" else 34
+        blk = w.reshape(-1, bb).copy()
+        d = blk[:, 0:2].copy().view(np.float16) * np.float16(2)
+        blk[:, 0:2] = d.view(np.uint8).reshape(-1, 2)
+        w2, s2 = blk.reshape(-1), None
+    y3 = gu.gemv(fmt, gu.upload(fmt, w2, s2, N, K), x, N, K)
+    assert np.array_equal(y3, 2 * y1)
+    # one-hot x -> column of the unpacked weights, bit for bit
+    out32 = torch.empty(N * K, dtype=torch.float32, device="cuda")
+    lq.lq_dequant_f32(gu.FMT[fmt], Wd, out32, N, K)
+    torch.cuda.synchronize()
+    full = out32.cpu().numpy().reshape(N, K)
+    for k in (0, 1, 15, 16, 31, 32, 63, K - 1):
+        e = np.zeros(K, np.float32)
+        e[k] = 1.0
+        yk = gu.gemv(fmt, Wd, e, N, K)
+        assert np.array_equal(yk.view(np.uint32), full[:, k].view(np.uint32)), k
+
+
+def test_gemv_zero_codes():
+    """Q4_0 codes all 8 (and Q8_0 codes all 0) give exactly zero."""
+    N, K = 64, 896
+    for fmt, byte in (("q4_0", 0x88), ("q8_0", 0x00)):
+        say("gemv zero codes", fmt)
+        w, _ = make(fmt, 5, N, K)
+        bb = 18 if fmt == "q4_0" else 34
+        blk = w.reshape(-1, bb).copy()
+        blk[:, 2:] = byte
+        y = gu.gemv(fmt, gu.upload(fmt, blk.reshape(-1), None, N, K),
+                    lqgen.activations(3, K, np.float32), N, K)
+        assert np.all(y == 0)
+
+
+# ------------------------------------------------ workloads at full size ----
+
+def _run_workload_rows(oracle, wl, sample=None, batch=True):
+    mats = [(m, *m.generate()) for m in wl.mats]
+    xs = {k: wl.x(k) for k in wl.xs}
+    descs, outs, devs = [], [], []
+    for m, w, s in mats:
+        Wd = gu.upload(m.fmt, w, s, m.N, m.K)
+        xd = to_device(xs[m.xkey])
+        y = gu.guarded(m.N)
+        devs.append((Wd, xd))
+        descs.append((gu.FMT[m.fmt], Wd, xd, y, m.N, m.K))
+        outs.append(y)
+    if batch:
+        lq.lq_gemv_batch(descs)
+    else:
+        for d in descs:
+            lq.lq_gemv(d[0], d[1], d[2], d[3], d[4], d[5])
+    torch.cuda.synchronize()
+    worst = 0.0
+    for (m, w, s), y in zip(mats, outs):
+        gu.check_guard(y, m.N)
+        yy = y[:m.N].cpu().numpy()
+        if sample and m.N > sample:
+            rng = np.random.default_rng(m.seed)
+            rows = np.unique(np.concatenate([[0, 1, m.N - 2, m.N - 1], rng.integers(0, m.N, sample)]))
+            yr, S = oracle.gemv(ORACLE_FMT[m.fmt], w, s, xs[m.xkey], m.N, m.K, rows=rows)
+            r = gu.ratio(yy[rows], yr, S, gu.GEMV_REL, gu.GEMV_ABS)
+        else:
+            yr, S = oracle.gemv(ORACLE_FMT[m.fmt], w, s, xs[m.xkey], m.N, m.K)
+            r = gu.ratio(yy, yr, S, gu.GEMV_REL, gu.GEMV_ABS)
+        assert r <= 1.0, (wl.name, m.name, r)
+        worst = max(worst, r)
+    return worst
+
+
+@pytest.mark.slow
+def test_workload_q4_0_2560x960(oracle):
+    say("workload q4_0 2560x960")
+    _run_workload_rows(oracle, lqgen.q4_0_ffn_2560x960(), batch=False)
+
+
+@pytest.mark.slow
+def test_workload_q8_0_layer(oracle):
+    say("workload q8_0 decoder layer (grouped launch)")
+    _run_workload_rows(oracle, lqgen.q8_0_layer_2048(0), batch=True)
+
+
+@pytest.mark.slow
+def test_workload_q4_0_lm_head(oracle):
+    say("workload q4_0 LM head 151936x896 + FFN")
+    _run_workload_rows(oracle, lqgen.q4_0_lmhead_151936x896(), sample=8192, batch=False)
+
+
+@pytest.mark.slow
+def test_workload_i8b64_layers(oracle):
+    for layer in (0, 21):
+        say("workload i8b64 TinyLlama layer", layer)
+        _run_workload_rows(oracle, lqgen.i8b64_tinyllama_layer(layer), sample=1024, batch=True)
+
+
+# ---------------------------------------------------------------- GEMM ----
+
+GEMM_SHAPES = [(16, 64, 64), (5, 33, 96), (130, 129, 160), (1, 128, 64), (200, 300, 2048),
+               (512, 256, 1024), (64, 2048, 1376)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_parity(oracle, M, N, K):
+    say("gemm", M, N, K)
+    w, _ = make("q4_0", 77 + N, N, K)
+    X = lqgen.activations(55 + M, M * K, np.float16).reshape(M, K)
+    Wd = gu.upload("q4_0", w, None, N, K)
+    Y = gu.gemm(Wd, X, M, N, K)
+    Yr, S = oracle.gemm(0, w, None, X, M, N, K)
+    assert gu.ratio(Y, Yr, S, gu.GEMM_REL, gu.GEMM_ABS) <= 1.0
+    # against the fp16 tile contract the fp32-accumulation error is all that is left
+    Yt, St = oracle.gemm(0, w, None, X, M, N, K, round_w_f16=True)
+    assert gu.ratio(Y, Yt, St, 1e-4, 1e-6) <= 1.0
+
+
+def test_gemm_one_hot_rows_pin_tile():
+    """X[m] = e_{k_m} gives Y[m, :] = RN_fp16 of weight column k_m, bit for bit."""
+    M, N, K = 40, 160, 320
+    say("gemm one-hot", M, N, K)
+    w, _ = make("q4_0", 4, N, K)
+    Wd = gu.upload("q4_0", w, None, N, K)
+    ks = [(7 * m + 3) % K for m in range(M)]
+    X = np.zeros((M, K), np.float16)
+    for m, k in enumerate(ks):
+        X[m, k] = 1
+    Y = gu.gemm(Wd, X, M, N, K)
+    out16 = torch.empty(N * K, dtype=torch.uint16, device="cuda")
+    lq.lq_dequant_f16(lq.LQ_Q4_0, Wd, out16, N, K)
+    torch.cuda.synchronize()
+    W16 = out16.cpu().numpy().reshape(N, K).view(np.float16).astype(np.float32)
+    for m, k in enumerate(ks):
+        assert np.array_equal(Y[m].view(np.uint32), W16[:, k].view(np.uint32)), m
+
+
+def test_gemm_rows_match_gemv(oracle):
+    M, N, K = 48, 200, 2048
+    say("gemm rows vs gemv", M, N, K)
+    w, _ = make("q4_0", 8, N, K)
+    Wd = gu.upload("q4_0", w, None, N, K)
+    X = lqgen.activations(9, M * K, np.float16).reshape(M, K)
+    Y = gu.gemm(Wd, X, M, N, K)
+    for m in (0, 17, 47):
+        y = gu.gemv("q4_0", Wd, X[m], N, K)
+        _, S = oracle.gemv(0, w, None, X[m], N, K)
+        assert np.all(np.abs(Y[m].astype(np.float64) - y) <= gu.GEMM_REL * S + gu.GEMM_ABS), m
+
+
+def test_matmul_routes_by_token_count():
+    N, K = 96, 256
+    say("matmul routing")
+    w, _ = make("q4_0", 12, N, K)
+    Wd = gu.upload("q4_0", w, None, N, K)
+    x = lqgen.activations(13, K, np.float16)
+    y1 = gu.gemv("q4_0", Wd, x, N, K)
+    Y = gu.guarded(N)
+    lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(x), Y, 1, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(Y[:N].cpu().numpy(), y1)
+
+
+@pytest.mark.slow
+def test_workload_q4_0_prefill_ffn(oracle):
+    wl = lqgen.q4_0_prefill_ffn_2048x11008(512)
+    M = wl.M
+    for m in wl.mats:
+        say("gemm workload", m.name, M, m.N, m.K)
+        w, _ = m.generate()
+        X = wl.x(m.xkey)
+        Wd = gu.upload("q4_0", w, None, m.N, m.K)
+        Y = gu.gemm(Wd, X, M, m.N, m.K)
+        rng = np.random.default_rng(m.seed)
+        ms = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 511], rng.integers(0, M, 25)]))
+        ns = np.unique(np.concatenate([[0, 1, 127, 128, m.N - 1], rng.integers(0, m.N, 120)]))
+        Yr, S = oracle.gemm(0, w, None, X, M, m.N, m.K, ms=ms, ns=ns)
+        r = gu.ratio(Y[np.ix_(ms, ns)], Yr, S, gu.GEMM_REL, gu.GEMM_ABS)
+        assert r <= 1.0, (m.name, r)
