@@ -90,7 +90,8 @@ lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
 }
 
 // Fill one descriptor of a grouped GEMV launch.
-lq::GemvDesc make_desc(const lq_gemv_desc& d, int rows_per_iter) {
+lq::GemvDesc make_desc(const lq_gemv_desc& d, const lq::GemvConfig& cfg, int64_t iter0,
+                       int32_t x_off) {
     lq::GemvDesc g;
     g.codes = static_cast<const uint8_t*>(d.W);
     g.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(d.fmt, d.N, d.K));
@@ -99,30 +100,80 @@ lq::GemvDesc make_desc(const lq_gemv_desc& d, int rows_per_iter) {
     g.N = int32_t(d.N);
     g.nu = int32_t(d.K / 32);
     g.xdt = d.xdt;
-    g.iters = int32_t((d.N + rows_per_iter - 1) / rows_per_iter);
+    g.nchunks = (g.nu + cfg.tp - 1) / cfg.tp;
+    g.iters = int32_t((d.N + cfg.rows_per_iter - 1) / cfg.rows_per_iter);
+    g.iter0 = int32_t(iter0);
+    g.x_off = x_off;
+    g.pad = 0;
     return g;
 }
 
+// Launch one group of descriptors that share a kernel and fit its limits
+// (kMaxBatch matrices, kGemvXLdsFloats staged activations).
+lq_status launch_one(int fmt, const lq::GemvConfig& cfg, const std::vector<const lq_gemv_desc*>& g,
+                     int cus, hipStream_t stream) {
+    lq::GemvBatchArgs a = {};
+    int64_t iters = 0;
+    int32_t lds_floats = 0;
+    for (size_t i = 0; i < g.size(); ++i) {
+        const lq_gemv_desc& d = *g[i];
+        int32_t x_off = 0;
+        if (!cfg.x_global) {
+            int j = 0;
+            while (j < a.nx && !(a.xs[j].x == d.x && a.xs[j].K == d.K && a.xs[j].xdt == d.xdt)) ++j;
+            if (j == a.nx) {
+                a.xs[j].x = d.x;
+                a.xs[j].K = int32_t(d.K);
+                a.xs[j].xdt = d.xdt;
+                a.xs[j].lds_off = lds_floats;
+                a.xs[j].pad = 0;
+                lds_floats += int32_t(d.K);
+                ++a.nx;
+            }
+            x_off = a.xs[j].lds_off;
+        }
+        a.d[i] = make_desc(d, cfg, iters, x_off);
+        iters += a.d[i].iters;
+    }
+    if (iters > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
+    a.count = int32_t(g.size());
+    a.total_iters = int32_t(iters);
+    // A few resident workgroups per CU take the row iterations grid-stride:
+    // enough loads in flight to saturate HBM without oversubscribing.
+    const int64_t grid = std::min<int64_t>(iters, int64_t(cus) * LQ_GEMV_WGS_PER_CU);
+    const hipError_t e = lq::launch_gemv(fmt, cfg, a, int(grid), size_t(lds_floats) * sizeof(float), stream);
+    if (e != hipSuccess) return hip_fail(e, "GEMV launch");
+    return LQ_OK;
+}
+
+// Split one kernel's descriptors (in order) into launches within its limits.
 lq_status launch_group(int fmt, const lq::GemvConfig& cfg, const std::vector<const lq_gemv_desc*>& g,
                        int cus, hipStream_t stream) {
-    for (size_t base = 0; base < g.size(); base += lq::kMaxBatch) {
-        lq::GemvBatchArgs a = {};
-        const size_t cnt = std::min(g.size() - base, size_t(lq::kMaxBatch));
-        a.count = int32_t(cnt);
-        a.prefix[0] = 0;
-        for (size_t i = 0; i < cnt; ++i) {
-            a.d[i] = make_desc(*g[base + i], cfg.rows_per_iter);
-            a.prefix[i + 1] = a.prefix[i] + a.d[i].iters;
+    std::vector<const lq_gemv_desc*> cur;
+    struct XKey { const void* x; int64_t K; int32_t xdt; };
+    std::vector<XKey> xs;   // distinct activations of `cur` (same key as launch_one)
+    int64_t lds = 0;
+    for (const lq_gemv_desc* d : g) {
+        bool seen = false;
+        for (const auto& x : xs) seen = seen || (x.x == d->x && x.K == d->K && x.xdt == d->xdt);
+        const int64_t add = (cfg.x_global || seen) ? 0 : d->K;
+        if (!cur.empty() && (cur.size() == size_t(lq::kMaxBatch) || lds + add > lq::kGemvXLdsFloats)) {
+            LQ_TRY(launch_one(fmt, cfg, cur, cus, stream));
+            cur.clear();
+            xs.clear();
+            lds = 0;
         }
-        const int total = a.prefix[cnt];
-        // Enough workgroups to fill every CU several times over, each walking
-        // an equal share of the row iterations.
-        const int cap = cus * 8;
-        const int per = (total + cap - 1) / cap;
-        const int grid = (total + per - 1) / per;
-        const hipError_t e = lq::launch_gemv(fmt, cfg, a, grid, stream);
-        if (e != hipSuccess) return hip_fail(e, "GEMV launch");
+        if (!cfg.x_global) {
+            bool again = false;
+            for (const auto& x : xs) again = again || (x.x == d->x && x.K == d->K && x.xdt == d->xdt);
+            if (!again) {
+                xs.push_back(XKey{d->x, d->K, d->xdt});
+                lds += d->K;
+            }
+        }
+        cur.push_back(d);
     }
+    if (!cur.empty()) LQ_TRY(launch_one(fmt, cfg, cur, cus, stream));
     return LQ_OK;
 }
 
@@ -211,12 +262,12 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream) 
     std::vector<bool> done(size_t(count), false);
     for (int32_t i = 0; i < count; ++i) {
         if (done[i]) continue;
-        const lq::GemvConfig cfg = lq::gemv_config(int(descs[i].K / 32));
+        const lq::GemvConfig cfg = lq::gemv_config(descs[i].fmt, int(descs[i].K / 32));
         std::vector<const lq_gemv_desc*> group;
         for (int32_t j = i; j < count; ++j) {
             if (done[j] || descs[j].fmt != descs[i].fmt) continue;
-            const lq::GemvConfig cj = lq::gemv_config(int(descs[j].K / 32));
-            if (cj.tp != cfg.tp || cj.upl != cfg.upl) continue;
+            const lq::GemvConfig cj = lq::gemv_config(descs[j].fmt, int(descs[j].K / 32));
+            if (cj.tp != cfg.tp || cj.x_global != cfg.x_global) continue;
             group.push_back(&descs[j]);
             done[j] = true;
         }

@@ -4,25 +4,35 @@
 // Decode streams every weight once, so the kernel is bound by HBM bandwidth
 // ("oxinfer" page, "Performance": decode is memory-bandwidth bound and its
 // speed is set by bytes per token).  Design for gfx950:
-//   * A team of TP lanes (16..256) works on one row at a time.  Lane t of a
-//     team owns the 32-weight units t, t + TP, ... of every row it touches and
-//     keeps those activations in VGPRs for the whole kernel, so x is read from
-//     L2 once per workgroup and never re-read per row.
-//   * Each lane issues one 128-bit load per unit and row (two for int8
-//     codes); consecutive lanes read consecutive 16-byte blocks, so a wave's
-//     load covers one contiguous span of the code plane.  All loads of an
-//     iteration (RPI rows x UPL units) are issued before any arithmetic.
+//   * One launch covers up to 16 matrices (for example every projection of a
+//     decoder layer).  Their rows are cut into row iterations of RPI rows per
+//     team, each walked in chunks of TP 32-weight units (one step per chunk).
+//     A persistent grid (a few workgroups per CU) takes the row iterations
+//     grid-stride, so at any moment all workgroups stream neighbouring rows
+//     (DRAM-friendly) and every CU stays busy to the end.
+//   * All activation vectors of the launch (de-duplicated by the host) are
+//     copied into LDS as fp32 once, before the main loop: the loop itself has
+//     no barrier and no activation load from global memory.  Each lane copies
+//     its unit's 32 values into VGPRs when the matrix or chunk changes.
+//   * A team of TP lanes (16, 32 or 64: the smallest that covers a row; long
+//     rows are walked in chunks of 64 units) works on one row at a time; lane
+//     t of a team owns unit t of the chunk.  Consecutive lanes read
+//     consecutive 16-byte code blocks, so each wave load is one contiguous
+//     span of the code plane, issued as 128-bit non-temporal loads.
+//   * A ring of register buffers keeps the loads of the next steps in flight
+//     while the current step computes.
 //   * Q4_0 nibbles become exact fp16 values (q - 8) with one v_and_or_b32
 //     (nibble into an fp16 mantissa under exponent 2^10) and one v_pk_add_f16
 //     per two weights; v_fma_mix_f32 then multiplies that fp16 by the fp32
-//     activation into an fp32 accumulator.  About 2.1 VALU ops per weight.
+//     activation into an fp32 accumulator.
 //   * int8 codes use sign-extending SDWA byte selects into v_cvt_f32_i32 and an
-//     fp32 FMA: 2 VALU ops per weight.
+//     fp32 FMA.
 //   * The block scale multiplies the unit's partial sum once (per block, not
 //     per weight).  Partial sums of a row are combined across the team with
 //     a transposed butterfly: each halving step exchanges half of the rows'
-//     partials, so RPI rows cost about RPI + log2(TP) shuffles instead of
-//     RPI * log2(TP).  Teams wider than a wave finish through LDS.
+//     partials, so RPI rows cost about RPI + log2(TP) exchanges instead of
+//     RPI * log2(TP), and every exchange is a VALU lane permute (DPP or
+//     permlane swap), never an LDS round trip.
 #include "lq_internal.h"
 
 namespace lq {
@@ -30,6 +40,7 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
@@ -72,6 +83,23 @@ __device__ __forceinline__ float dot_q4_0(const u32x4 c, const float (&x)[32]) {
     return __builtin_fmaf(s_hi, 0.0625f, s_lo);
 }
 
+// Signed byte n of a dword to fp32 in one VALU op (SDWA byte select with
+// sign extension).  Written out so the compiler cannot split each loaded
+// dword into four shifted copies ahead of use.
+#define LQ_SBYTE_TO_F32(NAME, SEL)                                                       \
+    __device__ __forceinline__ float NAME(uint32_t d) {                                  \
+        float r;                                                                         \
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:" SEL \
+            : "=v"(r)                                                                    \
+            : "v"(d));                                                                   \
+        return r;                                                                        \
+    }
+LQ_SBYTE_TO_F32(sbyte0, "BYTE_0")
+LQ_SBYTE_TO_F32(sbyte1, "BYTE_1")
+LQ_SBYTE_TO_F32(sbyte2, "BYTE_2")
+LQ_SBYTE_TO_F32(sbyte3, "BYTE_3")
+#undef LQ_SBYTE_TO_F32
+
 // Sum over 32 int8 codes (two 16-byte loads, element order) of c_e * x_e.
 __device__ __forceinline__ float dot_i8(const u32x4 c0, const u32x4 c1, const float (&x)[32]) {
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
@@ -79,10 +107,10 @@ __device__ __forceinline__ float dot_i8(const u32x4 c0, const u32x4 c1, const fl
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t d = w[i];
-        s0 = __builtin_fmaf((float)(int8_t)(d), x[4 * i + 0], s0);
-        s1 = __builtin_fmaf((float)(int8_t)(d >> 8), x[4 * i + 1], s1);
-        s0 = __builtin_fmaf((float)(int8_t)(d >> 16), x[4 * i + 2], s0);
-        s1 = __builtin_fmaf((float)(int8_t)(d >> 24), x[4 * i + 3], s1);
+        s0 = __builtin_fmaf(sbyte0(d), x[4 * i + 0], s0);
+        s1 = __builtin_fmaf(sbyte1(d), x[4 * i + 1], s1);
+        s0 = __builtin_fmaf(sbyte2(d), x[4 * i + 2], s0);
+        s1 = __builtin_fmaf(sbyte3(d), x[4 * i + 3], s1);
     }
     return s0 + s1;
 }
@@ -121,30 +149,74 @@ __device__ __forceinline__ void load_x_unit(const void* x, int xdt, int u, bool 
     }
 }
 
+// Value held by this lane's exchange partner across lane bit OFF, with VALU
+// lane permutes only (no LDS round trip): DPP quad permutes for bits 0 and 1,
+// DPP half-row / row mirrors for bits 2 and 3 (lane i <-> 7-i, 15-i: partner
+// differs in that bit), and the gfx950 permlane16 / permlane32 swaps for
+// bits 4 and 5.  lt is the lane index inside an aligned team (its low bits
+// equal the wave lane's).
+template <int OFF>
+__device__ __forceinline__ float xor_partner(float v, int lt) {
+    const uint32_t u = __float_as_uint(v);
+    uint32_t r;
+    if constexpr (OFF == 1) {
+        r = __builtin_amdgcn_update_dpp(0u, u, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    } else if constexpr (OFF == 2) {
+        r = __builtin_amdgcn_update_dpp(0u, u, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (OFF == 4) {
+        r = __builtin_amdgcn_update_dpp(0u, u, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    } else if constexpr (OFF == 8) {
+        r = __builtin_amdgcn_update_dpp(0u, u, 0x140, 0xF, 0xF, false);  // row_mirror
+    } else if constexpr (OFF == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        r = (lt & 16) ? p[0] : p[1];
+    } else {
+        static_assert(OFF == 32, "lane exchange offset must be 1..32");
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        r = (lt & 32) ? p[0] : p[1];
+    }
+    return __uint_as_float(r);
+}
+
+// One halving step of the transposed butterfly: lanes whose bit OFF is set
+// keep the upper half of the N live partials and send the lower half to their
+// partner, which does the opposite; each side adds what it receives.
+template <int N, int OFF, int RPI>
+__device__ __forceinline__ void halve(float (&v)[RPI], int lt) {
+    constexpr int H = N / 2;
+    const bool upper = (lt & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        const float send = upper ? v[i] : v[i + H];
+        const float keep = upper ? v[i + H] : v[i];
+        v[i] = keep + xor_partner<OFF>(send, lt);
+    }
+}
+
+template <int N, int OFF, int RPI>
+__device__ __forceinline__ void reduce_from(float (&v)[RPI], int lt) {
+    if constexpr (OFF >= 1) {
+        if constexpr (N > 1) {
+            halve<N, OFF, RPI>(v, lt);
+            reduce_from<N / 2, OFF / 2, RPI>(v, lt);
+        } else {
+            v[0] += xor_partner<OFF>(v[0], lt);
+            reduce_from<1, OFF / 2, RPI>(v, lt);
+        }
+    }
+}
+
 // Transposed butterfly over the TPW lanes of a team inside one wave: on entry
 // every lane holds RPI partials (one per row); on exit the lane whose bits
 // (TPW/2, TPW/4, ...) spell r holds the team's total for row r in v[0].
+// The partner of a lane differs from it in the bit being reduced, so the
+// halving decisions and the final row assignment depend only on the lane's
+// own bits, whichever partner permutation is used.
 template <int RPI, int TPW>
 __device__ __forceinline__ void team_reduce(float (&v)[RPI], int lt) {
-    int n = RPI;
-    int off = TPW / 2;
-#pragma unroll
-    for (int step = 0; (RPI >> step) > 1; ++step) {
-        const int h = n / 2;
-        const bool upper = (lt & off) != 0;
-#pragma unroll
-        for (int i = 0; i < RPI / 2; ++i) {
-            if (i < h) {
-                const float send = upper ? v[i] : v[i + h];
-                const float keep = upper ? v[i + h] : v[i];
-                v[i] = keep + __shfl_xor(send, off, 64);
-            }
-        }
-        n = h;
-        off >>= 1;
-    }
-#pragma unroll
-    for (; off >= 1; off >>= 1) v[0] += __shfl_xor(v[0], off, 64);
+    static_assert(RPI == 1 || RPI == 2 || RPI == 4 || RPI == 8, "RPI must be 1, 2, 4 or 8");
+    static_assert(TPW >= RPI && TPW <= 64, "a team needs RPI..64 lanes");
+    reduce_from<RPI, TPW / 2, RPI>(v, lt);
 }
 
 // Row index held by lane lt after team_reduce.
@@ -160,169 +232,279 @@ __device__ __forceinline__ int reduced_row(int lt) {
     return r;
 }
 
-template <int FMT, int TP, int UPL>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvBatchArgs args) {
-    constexpr int RPI = UPL == 1 ? 8 : (UPL == 2 ? 4 : 2);   // rows per team per iteration
-    constexpr int TEAMS = kGemvThreads / TP;
-    constexpr int ROWS = TEAMS * RPI;
-    constexpr int CW = FMT == kQ4_0 ? 1 : 2;                  // 16-byte loads per unit
-    constexpr int TPW = TP < 64 ? TP : 64;                    // team lanes inside one wave
-    constexpr int WAVES_PER_TEAM = TP / TPW;
+// LDS offset (in floats) of the v-th group of four activations of unit u.
+// Lanes of a wave read the same group v of consecutive units; rotating the
+// eight groups of a unit by u spreads those reads over all LDS banks instead
+// of one 128-byte column.
+__device__ __forceinline__ int x_slot(int u, int v) { return u * 32 + ((v + u) & 7) * 4; }
 
-    __shared__ float red[kGemvThreads / 64][RPI];
+// Position in a launch's work: global row iteration (over all matrices of
+// the launch, in order), the matrix it belongs to, its row iteration inside
+// that matrix, and the chunk of the row.
+struct Pos {
+    int gi;
+    int di;
+    int it;
+    int ch;
+};
+
+__device__ __forceinline__ Pos pos_of(const GemvBatchArgs& a, int gi) {
+    int di = 0;
+    while (di + 1 < a.count && gi >= a.d[di + 1].iter0) ++di;
+    return Pos{gi, di, gi - a.d[di].iter0, 0};
+}
+
+// Next step of this workgroup: the next chunk of the row, else the
+// workgroup's next row iteration: grid-stride (all workgroups stream
+// neighbouring rows at any moment) or, with LQ_GEMV_CONTIGUOUS, the next row
+// iteration of the workgroup's own contiguous range.
+#ifndef LQ_GEMV_CONTIGUOUS
+#define LQ_GEMV_CONTIGUOUS 0
+#endif
+__device__ __forceinline__ Pos advance(const GemvBatchArgs& a, const Pos& p, int it_end) {
+    if (p.ch + 1 < a.d[p.di].nchunks) return Pos{p.gi, p.di, p.it, p.ch + 1};
+    const int gi = p.gi + (LQ_GEMV_CONTIGUOUS ? 1 : int(gridDim.x));
+    if (gi >= it_end) return Pos{it_end, a.count, 0, 0};
+    if (gi - a.d[p.di].iter0 < a.d[p.di].iters) return Pos{gi, p.di, p.it + (gi - p.gi), 0};
+    return pos_of(a, gi);
+}
+
+// Scales stay as raw bits until the step is computed: converting them right
+// after the load would make the wave wait for the load there (vmcnt is in
+// order), stalling on the prefetch it has just issued.
+template <int FMT, int RPI>
+struct StepBuf {
+    static constexpr int CW = FMT == kQ4_0 ? 1 : 2;
+    u32x4 code[RPI][CW];
+    uint32_t sc[RPI];   // fp32 bits (int8 block-64) or fp16 bits (Q4_0 / Q8_0)
+    bool u_ok;          // this lane's unit lies inside the row
+};
+
+template <int FMT, int RPI>
+__device__ __forceinline__ float scale_of(const StepBuf<FMT, RPI>& b, int r) {
+    float s;
+    if (FMT == kI8B64) s = __uint_as_float(b.sc[r]);
+    else s = (float)__builtin_bit_cast(_Float16, uint16_t(b.sc[r]));
+    return b.u_ok ? s : 0.0f;
+}
+
+// Loads of one step: ordinary (compiler-visible) loads, so the compiler
+// tracks every destination register and places its waits itself.  Addresses
+// are a step-uniform base (scalar registers) plus a 32-bit lane offset inside
+// the step's rows.
+template <int FMT, int TP, int RPI>
+__device__ __forceinline__ void load_step(const GemvBatchArgs& a, const Pos& p, int team, int lt,
+                                          StepBuf<FMT, RPI>& b) {
+    constexpr int TEAMS = kGemvThreads / TP;
+    constexpr int CW = StepBuf<FMT, RPI>::CW;
+    const GemvDesc& D = a.d[p.di];
+    // Lanes past the end of a row or rows past N load a clamped (valid)
+    // address and get scale 0; their activations are 0 or their rows are not
+    // stored, so nothing they read reaches y.  No divergent branches.
+    const int u_raw = p.ch * TP + lt;
+    const bool u_ok = u_raw < D.nu;
+    const int u = u_ok ? u_raw : D.nu - 1;
+    const int row0 = p.it * TEAMS * RPI;
+    const int rows_left = D.N - 1 - row0;
+    const uint8_t* cbase = D.codes + size_t(row0) * size_t(D.nu) * (16 * CW);
+    const uint8_t* sbase = static_cast<const uint8_t*>(D.scales) +
+                           size_t(row0) * size_t(FMT == kI8B64 ? (D.nu / 2) * 4 : D.nu * 2);
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+        const int rel_raw = r * TEAMS + team;
+        const uint32_t rel = uint32_t(rel_raw <= rows_left ? rel_raw : rows_left);
+        const uint32_t unit = rel * uint32_t(D.nu) + uint32_t(u);
+        const u32x4* cp = reinterpret_cast<const u32x4*>(cbase + unit * (16u * CW));
+#pragma unroll
+        for (int c = 0; c < CW; ++c) b.code[r][c] = __builtin_nontemporal_load(cp + c);
+        if (FMT == kI8B64)
+            b.sc[r] = *reinterpret_cast<const uint32_t*>(
+                sbase + (rel * uint32_t(D.nu / 2) + uint32_t(u / 2)) * 4u);
+        else
+            b.sc[r] = *reinterpret_cast<const uint16_t*>(sbase + unit * 2u);
+    }
+    b.u_ok = u_ok;
+}
+
+// XG selects where activations come from: false = every activation vector of
+// the launch staged in LDS before the loop (the host keeps their total within
+// kGemvXLdsFloats), true = read from global memory per chunk (rows longer
+// than the LDS budget).
+template <int FMT, int TP, int RPI, bool XG>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(LQ_GEMV_WGS_PER_CU))) void gemv_kernel(const GemvBatchArgs args) {
+    constexpr int TEAMS = kGemvThreads / TP;
+    extern __shared__ float xs[];   // activations of every matrix of the launch (fp32)
 
     const int tid = threadIdx.x;
     const int team = tid / TP;
     const int lt = tid % TP;
-    const int wl = tid % TPW;
+    if (int(blockIdx.x) >= args.total_iters) return;
 
-    float xr[UPL][32];
-    int cur = -1;
-    const int total = args.prefix[args.count];
-
-    for (int it = blockIdx.x; it < total; it += gridDim.x) {
-        int di = 0;
-        while (di + 1 < args.count && it >= args.prefix[di + 1]) ++di;
-        const GemvDesc& D = args.d[di];
-        const int nu = D.nu;
-        const int nchunks = (nu + TP * UPL - 1) / (TP * UPL);
-        const int row0 = (it - args.prefix[di]) * ROWS;
-
-        float acc[RPI];
+    if (!XG) {
+        // Eight 16-byte loads in flight per thread before their LDS stores, so
+        // staging costs a few L2 round trips rather than one per load.
+        for (int j = 0; j < args.nx; ++j) {
+            const GemvXSrc& X = args.xs[j];
+            for (int i0 = tid * 4; i0 < X.K; i0 += kGemvThreads * 4 * 8) {
+                f32x4 v[8];
 #pragma unroll
-        for (int r = 0; r < RPI; ++r) acc[r] = 0.0f;
-
-        for (int ch = 0; ch < nchunks; ++ch) {
-            const int ubase = ch * TP * UPL;
-            if (nchunks > 1 || di != cur) {
-#pragma unroll
-                for (int j = 0; j < UPL; ++j) {
-                    const int u = ubase + lt + j * TP;
-                    load_x_unit(D.x, D.xdt, u, u < nu, xr[j]);
-                }
-                cur = di;
-            }
-            u32x4 code[RPI][UPL][CW];
-            float sc[RPI][UPL];
-#pragma unroll
-            for (int r = 0; r < RPI; ++r) {
-                const int row = row0 + r * TEAMS + team;
-#pragma unroll
-                for (int j = 0; j < UPL; ++j) {
-                    const int u = ubase + lt + j * TP;
-                    const bool ok = row < D.N && u < nu;
-                    const size_t unit = size_t(row) * size_t(nu) + size_t(u);
-#pragma unroll
-                    for (int c = 0; c < CW; ++c) code[r][j][c] = u32x4{0u, 0u, 0u, 0u};
-                    sc[r][j] = 0.0f;
-                    if (ok) {
-                        const u32x4* cp = reinterpret_cast<const u32x4*>(D.codes + unit * (16 * CW));
-#pragma unroll
-                        for (int c = 0; c < CW; ++c) code[r][j][c] = __builtin_nontemporal_load(cp + c);
-                        if (FMT == kI8B64) {
-                            sc[r][j] = static_cast<const float*>(D.scales)[size_t(row) * size_t(nu / 2) + u / 2];
-                        } else {
-                            const _Float16 h = static_cast<const _Float16*>(D.scales)[unit];
-                            sc[r][j] = (float)h;
-                        }
+                for (int q = 0; q < 8; ++q) {
+                    const int i = i0 + q * kGemvThreads * 4;
+                    const int ic = i < X.K ? i : X.K - 4;
+                    if (X.xdt == kF32) {
+                        v[q] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(X.x) + ic);
+                    } else {
+                        const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(X.x) + ic);
+                        const half2_t h0 = as_half2(h.x), h1 = as_half2(h.y);
+                        v[q] = f32x4{(float)h0.x, (float)h0.y, (float)h1.x, (float)h1.y};
                     }
                 }
-            }
 #pragma unroll
-            for (int r = 0; r < RPI; ++r) {
-#pragma unroll
-                for (int j = 0; j < UPL; ++j) {
-                    float s;
-                    if (FMT == kQ4_0) s = dot_q4_0(code[r][j][0], xr[j]);
-                    else s = dot_i8(code[r][j][0], code[r][j][CW - 1], xr[j]);
-                    acc[r] = __builtin_fmaf(sc[r][j], s, acc[r]);
+                for (int q = 0; q < 8; ++q) {
+                    const int i = i0 + q * kGemvThreads * 4;
+                    if (i < X.K)
+                        *reinterpret_cast<f32x4*>(xs + X.lds_off + x_slot(i / 32, (i % 32) / 4)) = v[q];
                 }
             }
         }
+        __syncthreads();
+    }
 
-        team_reduce<RPI, TPW>(acc, wl);
-        const int rr = reduced_row<RPI, TPW>(wl);
-        const bool owner = (wl % (TPW / RPI)) == 0;
-        if (WAVES_PER_TEAM == 1) {
-            const int row = row0 + rr * TEAMS + team;
-            if (owner && row < D.N) D.y[row] = acc[0];
-        } else {
-            const int wave = tid / 64;
-            if (owner) red[wave][rr] = acc[0];
-            __syncthreads();
-            if (tid < TEAMS * RPI) {
-                const int tm = tid / RPI;
-                const int r = tid % RPI;
-                float s = 0.0f;
+    float xr[32];
+    float acc[RPI];
+    int x_di = -1;          // matrix and chunk whose activations are in xr
+    int x_ch = -1;
+
+    auto process = [&](const Pos& p, StepBuf<FMT, RPI>& b) {
+        const GemvDesc& D = args.d[p.di];
+        if (p.di != x_di || p.ch != x_ch) {
+            const int u = p.ch * TP + lt;
+            if (u >= D.nu) {
 #pragma unroll
-                for (int w = 0; w < WAVES_PER_TEAM; ++w) s += red[tm * WAVES_PER_TEAM + w][r];
-                const int row = row0 + r * TEAMS + tm;
-                if (row < D.N) D.y[row] = s;
+                for (int e = 0; e < 32; ++e) xr[e] = 0.0f;
+            } else if (!XG) {
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    const f32x4 t = *reinterpret_cast<const f32x4*>(xs + D.x_off + x_slot(u, v));
+                    xr[4 * v + 0] = t.x;
+                    xr[4 * v + 1] = t.y;
+                    xr[4 * v + 2] = t.z;
+                    xr[4 * v + 3] = t.w;
+                }
+            } else {
+                load_x_unit(D.x, D.xdt, u, true, xr);
             }
-            __syncthreads();
+            x_di = p.di;
+            x_ch = p.ch;
+        }
+        if (p.ch == 0) {
+#pragma unroll
+            for (int r = 0; r < RPI; ++r) acc[r] = 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < RPI; ++r) {
+            float s;
+            if (FMT == kQ4_0) s = dot_q4_0(b.code[r][0], xr);
+            else s = dot_i8(b.code[r][0], b.code[r][StepBuf<FMT, RPI>::CW - 1], xr);
+            acc[r] = __builtin_fmaf(scale_of(b, r), s, acc[r]);
+            // Keep each row's unpacking next to its FMAs: interleaving the
+            // rows would hold every converted code of the step live at once.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (p.ch == D.nchunks - 1) {
+            float v[RPI];
+#pragma unroll
+            for (int r = 0; r < RPI; ++r) v[r] = acc[r];
+            team_reduce<RPI, TP>(v, lt);
+            const int rr = reduced_row<RPI, TP>(lt);
+            const int row = p.it * TEAMS * RPI + rr * TEAMS + team;
+            if ((lt % (TP / RPI)) == 0 && row < D.N) D.y[row] = v[0];
+        }
+    };
+
+    // A ring of NB register buffers: while one step is computed, the loads of
+    // the next NB-1 steps are in flight.  Every computed step is preceded by
+    // exactly one issued step (past the end the last step is re-read: cache
+    // hits), and the loop body is the same on every trip with its only exit
+    // leaving the loop, so the compiler's waits leave the younger steps in
+    // flight.
+    constexpr int NB = LQ_GEMV_NBUF;
+    StepBuf<FMT, RPI> buf[NB];
+    Pos q[NB];
+    bool qv[NB];
+#if LQ_GEMV_CONTIGUOUS
+    const int it_begin = int(int64_t(args.total_iters) * blockIdx.x / gridDim.x);
+    const int it_end = int(int64_t(args.total_iters) * (blockIdx.x + 1) / gridDim.x);
+#else
+    const int it_begin = int(blockIdx.x);
+    const int it_end = args.total_iters;
+#endif
+    if (it_begin >= it_end) return;
+    Pos issue = pos_of(args, it_begin);
+    bool issue_ok = true;
+    auto issue_next = [&](int bi) {
+        load_step<FMT, TP, RPI>(args, issue, team, lt, buf[bi]);
+        q[bi] = issue;
+        qv[bi] = issue_ok;
+        if (issue_ok) {
+            const Pos nx = advance(args, issue, it_end);
+            if (nx.gi < it_end) issue = nx;
+            else issue_ok = false;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) issue_next(i);
+    while (true) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            issue_next((k + NB - 1) % NB);
+            if (!qv[k]) goto finished;
+            process(q[k], buf[k]);
         }
     }
+finished:
+    return;
 }
 
-struct Cand { int tp, upl; };
-constexpr Cand kCands[] = {{16, 1}, {32, 1}, {64, 1}, {64, 2}, {64, 3},
-                           {128, 2}, {128, 3}, {256, 1}, {256, 2}, {256, 3}};
+template <int FMT, int RPI, bool XG>
+hipError_t launch_fmt(const GemvConfig& cfg, const GemvBatchArgs& args, int grid, size_t lds,
+                      hipStream_t s) {
+    switch (cfg.tp) {
+        case 16: hipLaunchKernelGGL((gemv_kernel<FMT, 16, RPI, XG>), dim3(grid), dim3(kGemvThreads), lds, s, args); break;
+        case 32: hipLaunchKernelGGL((gemv_kernel<FMT, 32, RPI, XG>), dim3(grid), dim3(kGemvThreads), lds, s, args); break;
+        case 64: hipLaunchKernelGGL((gemv_kernel<FMT, 64, RPI, XG>), dim3(grid), dim3(kGemvThreads), lds, s, args); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 template <int FMT>
-hipError_t launch_fmt(const GemvConfig& cfg, const GemvBatchArgs& args, int grid, hipStream_t s) {
-#define LQ_GEMV_CASE(TPv, UPLv)                                                         \
-    if (cfg.tp == TPv && cfg.upl == UPLv) {                                             \
-        hipLaunchKernelGGL((gemv_kernel<FMT, TPv, UPLv>), dim3(grid), dim3(kGemvThreads), \
-                           0, s, args);                                                 \
-        return hipGetLastError();                                                       \
-    }
-    LQ_GEMV_CASE(16, 1)
-    LQ_GEMV_CASE(32, 1)
-    LQ_GEMV_CASE(64, 1)
-    LQ_GEMV_CASE(64, 2)
-    LQ_GEMV_CASE(64, 3)
-    LQ_GEMV_CASE(128, 2)
-    LQ_GEMV_CASE(128, 3)
-    LQ_GEMV_CASE(256, 1)
-    LQ_GEMV_CASE(256, 2)
-    LQ_GEMV_CASE(256, 3)
-#undef LQ_GEMV_CASE
-    return hipErrorInvalidValue;
+hipError_t launch_x(const GemvConfig& cfg, const GemvBatchArgs& args, int grid, size_t lds,
+                    hipStream_t s) {
+    if (cfg.x_global) return launch_fmt<FMT, gemv_rpi(FMT), true>(cfg, args, grid, 0, s);
+    return launch_fmt<FMT, gemv_rpi(FMT), false>(cfg, args, grid, lds, s);
 }
 
 }  // namespace
 
-// Pick the team shape that wastes the fewest lane slots per row; a row longer
-// than 768 units (K > 24576) is processed in chunks, reloading activations.
-GemvConfig gemv_config(int nu) {
-    int best = -1;
-    long best_cost = 0;
-    for (int i = 0; i < int(sizeof(kCands) / sizeof(kCands[0])); ++i) {
-        const long slots = long(kCands[i].tp) * kCands[i].upl;
-        const long chunks = (nu + slots - 1) / slots;
-        // One chunk: fewest wasted lane slots.  Several chunks (activations
-        // re-read per chunk): fewest chunks first.
-        const long cost = chunks == 1 ? slots : (1L << 40) + chunks * (1L << 20) + slots * chunks;
-        if (best < 0 || cost < best_cost ||
-            (cost == best_cost && kCands[i].upl < kCands[best].upl)) {
-            best = i;
-            best_cost = cost;
-        }
-    }
+// Team width: the smallest of 16, 32, 64 lanes that covers a row's units in
+// one chunk; rows longer than 64 units are walked in chunks of 64.
+// Activations of rows longer than the LDS budget are read from global memory.
+GemvConfig gemv_config(int fmt, int nu) {
     GemvConfig c;
-    c.tp = kCands[best].tp;
-    c.upl = kCands[best].upl;
-    const int rpi = c.upl == 1 ? 8 : (c.upl == 2 ? 4 : 2);
-    c.rows_per_iter = (kGemvThreads / c.tp) * rpi;
+    c.tp = nu <= 16 ? 16 : (nu <= 32 ? 32 : 64);
+    c.rpi = gemv_rpi(fmt);
+    c.rows_per_iter = (kGemvThreads / c.tp) * c.rpi;
+    c.x_global = int64_t(nu) * 32 > kGemvXLdsFloats;
     return c;
 }
 
 hipError_t launch_gemv(int fmt, const GemvConfig& cfg, const GemvBatchArgs& args, int grid,
-                       hipStream_t stream) {
+                       size_t lds_bytes, hipStream_t stream) {
     switch (fmt) {
-        case kQ4_0: return launch_fmt<kQ4_0>(cfg, args, grid, stream);
-        case kQ8_0: return launch_fmt<kQ8_0>(cfg, args, grid, stream);
-        case kI8B64: return launch_fmt<kI8B64>(cfg, args, grid, stream);
+        case kQ4_0: return launch_x<kQ4_0>(cfg, args, grid, lds_bytes, stream);
+        case kQ8_0: return launch_x<kQ8_0>(cfg, args, grid, lds_bytes, stream);
+        case kI8B64: return launch_x<kI8B64>(cfg, args, grid, lds_bytes, stream);
         default: return hipErrorInvalidValue;
     }
 }
