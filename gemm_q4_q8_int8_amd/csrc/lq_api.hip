@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -29,11 +30,14 @@ bool fmt_ok(int32_t f) { return f == LQ_Q4_0 || f == LQ_Q8_0 || f == LQ_I8B64; }
 int32_t block_of(int32_t f) { return f == LQ_I8B64 ? 64 : (fmt_ok(f) ? 32 : 0); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 constexpr int64_t kMaxDim = 2147483647;
+// A 64-row tile spans at most 64 * K code bytes; kernels address inside a
+// tile with 32-bit offsets.
+constexpr int64_t kMaxK = int64_t(1) << 25;
 
 lq_status check_fmt_shape(int32_t fmt, int64_t N, int64_t K) {
     if (!fmt_ok(fmt)) return fail(LQ_ERR_FMT, "unknown weight format %d", fmt);
     if (N < 1 || N > kMaxDim) return fail(LQ_ERR_SHAPE, "N=%lld out of range [1, 2^31-1]", (long long)N);
-    if (K < 1 || K > kMaxDim) return fail(LQ_ERR_SHAPE, "K=%lld out of range [1, 2^31-1]", (long long)K);
+    if (K < 1 || K > kMaxK) return fail(LQ_ERR_SHAPE, "K=%lld out of range [1, 2^25]", (long long)K);
     if (K % block_of(fmt) != 0)
         return fail(LQ_ERR_SHAPE, "K=%lld is not a multiple of the block size %d", (long long)K, block_of(fmt));
     if (N * (K / 32) > (int64_t(1) << 40)) return fail(LQ_ERR_SHAPE, "matrix too large");
@@ -89,91 +93,76 @@ lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
     return LQ_OK;
 }
 
-// Fill one descriptor of a grouped GEMV launch.
-lq::GemvDesc make_desc(const lq_gemv_desc& d, const lq::GemvConfig& cfg, int64_t iter0,
-                       int32_t x_off) {
-    lq::GemvDesc g;
-    g.codes = static_cast<const uint8_t*>(d.W);
-    g.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(d.fmt, d.N, d.K));
-    g.x = d.x;
-    g.y = d.y;
-    g.N = int32_t(d.N);
-    g.nu = int32_t(d.K / 32);
-    g.xdt = d.xdt;
-    g.nchunks = (g.nu + cfg.tp - 1) / cfg.tp;
-    g.iters = int32_t((d.N + cfg.rows_per_iter - 1) / cfg.rows_per_iter);
-    g.iter0 = int32_t(iter0);
-    g.x_off = x_off;
-    g.pad = 0;
-    return g;
-}
-
-// Launch one group of descriptors that share a kernel and fit its limits
-// (kMaxBatch matrices, kGemvXLdsFloats staged activations).
-lq_status launch_one(int fmt, const lq::GemvConfig& cfg, const std::vector<const lq_gemv_desc*>& g,
-                     int cus, hipStream_t stream) {
-    lq::GemvBatchArgs a = {};
-    int64_t iters = 0;
-    int32_t lds_floats = 0;
-    for (size_t i = 0; i < g.size(); ++i) {
+// One grouped GEMV launch: up to kMaxBatch descriptors of one format and
+// activation dtype.  Chooses the K split S (workgroups per 64-row tile) so
+// the launch has about LQ_GEMV_WGS_PER_CU workgroups per CU, keeping at least
+// LQ_GEMV_MIN_UNITS units per wave and the partials within the scratch area.
+lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>& g, int cus,
+                       hipStream_t stream) {
+    const int n = int(g.size());
+    std::vector<int64_t> tiles(n), nu(n), S(n, 1);
+    int64_t total_tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        tiles[i] = (g[i]->N + lq::kTileRows - 1) / lq::kTileRows;
+        nu[i] = g[i]->K / lq::unit_elems(fmt);
+        total_tiles += tiles[i];
+    }
+    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
+    if (total_tiles < target) {
+        const int64_t want = (target + total_tiles - 1) / total_tiles;
+        int64_t part = 0, cnt = 0;
+        for (int i = 0; i < n; ++i) {
+            const int64_t cap = std::max<int64_t>(1, nu[i] / (4 * LQ_GEMV_MIN_UNITS));
+            S[i] = std::min(want, cap);
+            if (S[i] > 1) {
+                part += S[i] * tiles[i] * lq::kTileRows;
+                cnt += tiles[i];
+            }
+        }
+        if (part > lq::kGemvPartFloats || cnt > lq::kGemvCounters) {
+            // Too large to split within the scratch area: no split at all
+            // (such matrices have enough tiles to fill the chip anyway).
+            for (int i = 0; i < n; ++i) S[i] = 1;
+        }
+    }
+    float* part = nullptr;
+    uint32_t* cntp = nullptr;
+    bool any_split = false;
+    for (int i = 0; i < n; ++i) any_split = any_split || S[i] > 1;
+    if (any_split) {
+        const hipError_t e = lq::gemv_scratch(&part, &cntp);
+        if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
+    }
+    lq::GemvArgs a = {};
+    int64_t wgs = 0, part_off = 0, cnt_off = 0;
+    for (int i = 0; i < n; ++i) {
         const lq_gemv_desc& d = *g[i];
-        int32_t x_off = 0;
-        if (!cfg.x_global) {
-            int j = 0;
-            while (j < a.nx && !(a.xs[j].x == d.x && a.xs[j].K == d.K && a.xs[j].xdt == d.xdt)) ++j;
-            if (j == a.nx) {
-                a.xs[j].x = d.x;
-                a.xs[j].K = int32_t(d.K);
-                a.xs[j].xdt = d.xdt;
-                a.xs[j].lds_off = lds_floats;
-                a.xs[j].pad = 0;
-                lds_floats += int32_t(d.K);
-                ++a.nx;
-            }
-            x_off = a.xs[j].lds_off;
+        lq::GemvDesc& o = a.d[i];
+        o.codes = static_cast<const uint8_t*>(d.W);
+        o.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(fmt, d.N, d.K));
+        o.x = d.x;
+        o.y = d.y;
+        o.N = int32_t(d.N);
+        o.nu = int32_t(nu[i]);
+        o.tiles = int32_t(tiles[i]);
+        o.S = int32_t(S[i]);
+        o.wg0 = int32_t(wgs);
+        o.pad = 0;
+        o.part = nullptr;
+        o.cnt = nullptr;
+        if (S[i] > 1) {
+            o.part = part + part_off;
+            o.cnt = cntp + cnt_off;
+            part_off += S[i] * tiles[i] * lq::kTileRows;
+            cnt_off += tiles[i];
         }
-        a.d[i] = make_desc(d, cfg, iters, x_off);
-        iters += a.d[i].iters;
+        wgs += tiles[i] * S[i];
+        if (wgs > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
     }
-    if (iters > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
-    a.count = int32_t(g.size());
-    a.total_iters = int32_t(iters);
-    // A few resident workgroups per CU take the row iterations grid-stride:
-    // enough loads in flight to saturate HBM without oversubscribing.
-    const int64_t grid = std::min<int64_t>(iters, int64_t(cus) * LQ_GEMV_WGS_PER_CU);
-    const hipError_t e = lq::launch_gemv(fmt, cfg, a, int(grid), size_t(lds_floats) * sizeof(float), stream);
+    a.count = n;
+    a.total_wgs = int32_t(wgs);
+    const hipError_t e = lq::launch_gemv(fmt, xdt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMV launch");
-    return LQ_OK;
-}
-
-// Split one kernel's descriptors (in order) into launches within its limits.
-lq_status launch_group(int fmt, const lq::GemvConfig& cfg, const std::vector<const lq_gemv_desc*>& g,
-                       int cus, hipStream_t stream) {
-    std::vector<const lq_gemv_desc*> cur;
-    struct XKey { const void* x; int64_t K; int32_t xdt; };
-    std::vector<XKey> xs;   // distinct activations of `cur` (same key as launch_one)
-    int64_t lds = 0;
-    for (const lq_gemv_desc* d : g) {
-        bool seen = false;
-        for (const auto& x : xs) seen = seen || (x.x == d->x && x.K == d->K && x.xdt == d->xdt);
-        const int64_t add = (cfg.x_global || seen) ? 0 : d->K;
-        if (!cur.empty() && (cur.size() == size_t(lq::kMaxBatch) || lds + add > lq::kGemvXLdsFloats)) {
-            LQ_TRY(launch_one(fmt, cfg, cur, cus, stream));
-            cur.clear();
-            xs.clear();
-            lds = 0;
-        }
-        if (!cfg.x_global) {
-            bool again = false;
-            for (const auto& x : xs) again = again || (x.x == d->x && x.K == d->K && x.xdt == d->xdt);
-            if (!again) {
-                xs.push_back(XKey{d->x, d->K, d->xdt});
-                lds += d->K;
-            }
-        }
-        cur.push_back(d);
-    }
-    if (!cur.empty()) LQ_TRY(launch_one(fmt, cfg, cur, cus, stream));
     return LQ_OK;
 }
 
@@ -224,14 +213,8 @@ lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales, voi
     LQ_TRY(check_ptr(codes, 16, "codes"));
     LQ_TRY(check_ptr(scales, 4, "scales"));
     LQ_TRY(check_ptr(dst, 16, "dst"));
-    const size_t cb = lq::code_plane_bytes(fmt, N, K);
-    const size_t sb = lq::scale_plane_bytes(fmt, N, K);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(dst, codes, cb, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "code plane copy");
-    e = hipMemcpyAsync(static_cast<uint8_t*>(dst) + lq::align256(cb), scales, sb, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "scale plane copy");
-    return LQ_OK;
+    const hipError_t e = lq::launch_pack_planes(fmt, codes, scales, dst, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "pack launch");
 }
 
 static lq_status dequant_common(int32_t fmt, const void* W, void* out, int64_t N, int64_t K,
@@ -257,21 +240,23 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream) 
     for (int32_t i = 0; i < count; ++i) LQ_TRY(check_gemv_desc(descs[i], i));
     int cus = 0;
     LQ_TRY(device_cus(&cus));
-    // Group descriptors that share a kernel (format and team shape), keeping
-    // their order, and launch each group in chunks of kMaxBatch.
+    // Group descriptors that share a kernel (format and activation dtype),
+    // keeping their order, and launch each group in chunks of kMaxBatch.
     std::vector<bool> done(size_t(count), false);
     for (int32_t i = 0; i < count; ++i) {
         if (done[i]) continue;
-        const lq::GemvConfig cfg = lq::gemv_config(descs[i].fmt, int(descs[i].K / 32));
-        std::vector<const lq_gemv_desc*> group;
+        std::vector<const lq_gemv_desc*> chunk;
         for (int32_t j = i; j < count; ++j) {
-            if (done[j] || descs[j].fmt != descs[i].fmt) continue;
-            const lq::GemvConfig cj = lq::gemv_config(descs[j].fmt, int(descs[j].K / 32));
-            if (cj.tp != cfg.tp || cj.x_global != cfg.x_global) continue;
-            group.push_back(&descs[j]);
+            if (done[j] || descs[j].fmt != descs[i].fmt || descs[j].xdt != descs[i].xdt) continue;
+            chunk.push_back(&descs[j]);
             done[j] = true;
+            if (chunk.size() == size_t(lq::kMaxBatch)) {
+                LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, chunk, cus, static_cast<hipStream_t>(stream)));
+                chunk.clear();
+            }
         }
-        LQ_TRY(launch_group(descs[i].fmt, cfg, group, cus, static_cast<hipStream_t>(stream)));
+        if (!chunk.empty())
+            LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, chunk, cus, static_cast<hipStream_t>(stream)));
     }
     return LQ_OK;
 }

@@ -1,8 +1,11 @@
 // Layout conversion and exact unpacking.
 //
 //   repack_gguf: GGUF array-of-blocks (fp16 scale then codes, 18 or 34 bytes
-//   per block, only 2-byte aligned) -> the packed split layout whose code
-//   plane gives every block an aligned 16- or 32-byte slot.  Pure byte moves.
+//   per block, only 2-byte aligned) -> the tiled packed layout (64-row tiles,
+//   unit-major, each 16-byte code part of a unit stored for the tile's rows
+//   side by side).  Pure byte moves.
+//
+//   pack_planes: row-major code and scale planes -> the same tiled layout.
 //
 //   dequant: the unpacked-weight contract.  fp32 output is RN_fp32(w): exact
 //   for Q4_0 / Q8_0 (small integer times an fp16 scale always fits fp32) and a
@@ -12,7 +15,7 @@
 //   bits, so it is rounded to fp16 in integer arithmetic (one rounding, round
 //   to nearest even, gradual underflow) rather than through fp32.
 //
-// One thread handles one 32-weight unit.  These kernels run once per weight
+// One thread handles one block (repack, pack) or 32 weights (dequant).  These kernels run once per weight
 // upload or inside tests; they are not on the timed decode path.
 #include "lq_internal.h"
 
@@ -26,16 +29,16 @@ constexpr int kThreads = 256;
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void repack_kernel(const uint16_t* __restrict__ src,
-                                                          uint8_t* __restrict__ dst,
-                                                          int64_t nblocks, size_t scale_off) {
+                                                          uint8_t* __restrict__ dst, int64_t N,
+                                                          int64_t nu, size_t scale_off) {
     constexpr int HW = FMT == kQ4_0 ? 9 : 17;   // 16-bit words per GGUF block
-    constexpr int CV = FMT == kQ4_0 ? 1 : 2;    // 16-byte code vectors per block
+    constexpr int CV = unit_parts(FMT);         // 16-byte code parts per block
     const int64_t b = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-    if (b >= nblocks) return;
+    if (b >= N * nu) return;
+    const int64_t row = b / nu;
+    const TiledPos pos = tiled_pos(FMT, N, nu, row, b - row * nu);
     const uint16_t* s = src + b * HW;
-    uint16_t* scales = reinterpret_cast<uint16_t*>(dst + scale_off);
-    scales[b] = s[0];
-    u32x4* codes = reinterpret_cast<u32x4*>(dst) + b * CV;
+    reinterpret_cast<uint16_t*>(dst + scale_off)[pos.scale] = s[0];
 #pragma unroll
     for (int v = 0; v < CV; ++v) {
         u32x4 t;
@@ -43,8 +46,30 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(const uint16_t* __rest
         t.y = uint32_t(s[1 + 8 * v + 2]) | (uint32_t(s[1 + 8 * v + 3]) << 16);
         t.z = uint32_t(s[1 + 8 * v + 4]) | (uint32_t(s[1 + 8 * v + 5]) << 16);
         t.w = uint32_t(s[1 + 8 * v + 6]) | (uint32_t(s[1 + 8 * v + 7]) << 16);
-        codes[v] = t;
+        *reinterpret_cast<u32x4*>(dst + pos.code + size_t(v) * pos.part_stride) = t;
     }
+}
+
+// Row-major code and scale planes -> tiled layout: one thread per unit.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        uint8_t* __restrict__ dst, int64_t N,
+                                                        int64_t nu, size_t scale_off) {
+    constexpr int CV = unit_parts(FMT);
+    constexpr int SB = scale_bytes(FMT);
+    const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (g >= N * nu) return;
+    const int64_t row = g / nu;
+    const TiledPos pos = tiled_pos(FMT, N, nu, row, g - row * nu);
+    const u32x4* src = reinterpret_cast<const u32x4*>(codes) + g * CV;
+#pragma unroll
+    for (int v = 0; v < CV; ++v)
+        *reinterpret_cast<u32x4*>(dst + pos.code + size_t(v) * pos.part_stride) = src[v];
+    if constexpr (SB == 2)
+        reinterpret_cast<uint16_t*>(dst + scale_off)[pos.scale] = reinterpret_cast<const uint16_t*>(scales)[g];
+    else
+        reinterpret_cast<uint32_t*>(dst + scale_off)[pos.scale] = reinterpret_cast<const uint32_t*>(scales)[g];
 }
 
 // RN_fp16(c * s) for an int8 code c and an fp32 scale s, from the exact
@@ -87,17 +112,21 @@ __device__ uint16_t rn16_code_times_f32(int c, float s) {
 
 template <int FMT, bool F16>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ W,
-                                                           void* __restrict__ out,
-                                                           int64_t nunits, int nu,
-                                                           size_t scale_off) {
+                                                           void* __restrict__ out, int64_t N,
+                                                           int nh, size_t scale_off) {
+    // One thread per 32 weights: row `row`, 32-element group h of nh.
     const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-    if (g >= nunits) return;
-    const int64_t row = g / nu;
-    const int u = int(g % nu);
-    const int64_t K = int64_t(nu) * 32;
+    if (g >= N * nh) return;
+    const int64_t row = g / nh;
+    const int u = int(g % nh);                      // 32-element group
+    const int64_t K = int64_t(nh) * 32;
+    constexpr int GPU_ = unit_elems(FMT) / 32;      // groups per unit
+    const int64_t nu = nh / GPU_;
+    const TiledPos pos = tiled_pos(FMT, N, nu, row, u / GPU_);
+    const int part0 = (u % GPU_) * 2;               // int8: two 16-byte parts per group
     int code[32];
     if (FMT == kQ4_0) {
-        const u32x4 c = reinterpret_cast<const u32x4*>(W)[g];
+        const u32x4 c = *reinterpret_cast<const u32x4*>(W + pos.code);
         const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -106,16 +135,16 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
             code[j + 16] = int(byte >> 4) - 8;     // element j + 16: high nibble
         }
     } else {
-        const u32x4* cp = reinterpret_cast<const u32x4*>(W) + 2 * g;
-        const u32x4 c0 = cp[0], c1 = cp[1];
+        const u32x4 c0 = *reinterpret_cast<const u32x4*>(W + pos.code + size_t(part0) * pos.part_stride);
+        const u32x4 c1 = *reinterpret_cast<const u32x4*>(W + pos.code + size_t(part0 + 1) * pos.part_stride);
         const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
         for (int j = 0; j < 32; ++j) code[j] = int(int8_t((w[j / 4] >> (8 * (j % 4))) & 0xFFu));
     }
     if (!F16) {
         float s;
-        if (FMT == kI8B64) s = reinterpret_cast<const float*>(W + scale_off)[row * (nu / 2) + u / 2];
-        else s = float(reinterpret_cast<const _Float16*>(W + scale_off)[g]);
+        if (FMT == kI8B64) s = reinterpret_cast<const float*>(W + scale_off)[pos.scale];
+        else s = float(reinterpret_cast<const _Float16*>(W + scale_off)[pos.scale]);
         f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * K + int64_t(u) * 32);
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
@@ -129,11 +158,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     } else {
         uint16_t h[32];
         if (FMT == kI8B64) {
-            const float s = reinterpret_cast<const float*>(W + scale_off)[row * (nu / 2) + u / 2];
+            const float s = reinterpret_cast<const float*>(W + scale_off)[pos.scale];
 #pragma unroll
             for (int j = 0; j < 32; ++j) h[j] = rn16_code_times_f32(code[j], s);
         } else {
-            const _Float16 d = reinterpret_cast<const _Float16*>(W + scale_off)[g];
+            const _Float16 d = reinterpret_cast<const _Float16*>(W + scale_off)[pos.scale];
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
                 // exact fp16 code times fp16 scale: one correctly rounded fp16 product
@@ -160,27 +189,44 @@ int blocks_for(int64_t n) { return int((n + kThreads - 1) / kThreads); }
 
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,
                               hipStream_t stream) {
-    const int64_t nblocks = N * (K / 32);
+    const int64_t nu = K / 32;
     const size_t off = align256(code_plane_bytes(fmt, N, K));
     const uint16_t* s = static_cast<const uint16_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
+    const dim3 grid(blocks_for(N * nu));
     if (fmt == kQ4_0)
-        hipLaunchKernelGGL(repack_kernel<kQ4_0>, dim3(blocks_for(nblocks)), dim3(kThreads), 0, stream, s, d, nblocks, off);
+        hipLaunchKernelGGL(repack_kernel<kQ4_0>, grid, dim3(kThreads), 0, stream, s, d, N, nu, off);
     else if (fmt == kQ8_0)
-        hipLaunchKernelGGL(repack_kernel<kQ8_0>, dim3(blocks_for(nblocks)), dim3(kThreads), 0, stream, s, d, nblocks, off);
+        hipLaunchKernelGGL(repack_kernel<kQ8_0>, grid, dim3(kThreads), 0, stream, s, d, N, nu, off);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
+hipError_t launch_pack_planes(int fmt, const void* codes, const void* scales, void* dst, int64_t N,
+                              int64_t K, hipStream_t stream) {
+    const int64_t nu = K / unit_elems(fmt);
+    const size_t off = align256(code_plane_bytes(fmt, N, K));
+    const uint8_t* c = static_cast<const uint8_t*>(codes);
+    const uint8_t* s = static_cast<const uint8_t*>(scales);
+    uint8_t* d = static_cast<uint8_t*>(dst);
+    const dim3 grid(blocks_for(N * nu));
+    switch (fmt) {
+        case kQ4_0: hipLaunchKernelGGL(pack_kernel<kQ4_0>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
+        case kQ8_0: hipLaunchKernelGGL(pack_kernel<kQ8_0>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
+        case kI8B64: hipLaunchKernelGGL(pack_kernel<kI8B64>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_dequant(int fmt, bool to_f16, const void* W, void* out, int64_t N, int64_t K,
                           hipStream_t stream) {
-    const int nu = int(K / 32);
-    const int64_t nunits = N * nu;
+    const int nh = int(K / 32);
     const size_t off = align256(code_plane_bytes(fmt, N, K));
     const uint8_t* w = static_cast<const uint8_t*>(W);
-    const dim3 grid(blocks_for(nunits)), block(kThreads);
-#define LQ_DQ(F, H) hipLaunchKernelGGL((dequant_kernel<F, H>), grid, block, 0, stream, w, out, nunits, nu, off)
+    const dim3 grid(blocks_for(N * nh)), block(kThreads);
+#define LQ_DQ(F, H) hipLaunchKernelGGL((dequant_kernel<F, H>), grid, block, 0, stream, w, out, N, nh, off)
     switch (fmt * 2 + (to_f16 ? 1 : 0)) {
         case kQ4_0 * 2 + 0: LQ_DQ(kQ4_0, false); break;
         case kQ4_0 * 2 + 1: LQ_DQ(kQ4_0, true); break;

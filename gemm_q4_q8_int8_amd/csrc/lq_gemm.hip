@@ -68,7 +68,6 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(const uint8_t* __re
     const int wn = wave % 2;
     const int nb = K / 32;
 
-    const u32x4* codes = reinterpret_cast<const u32x4*>(W);
     const _Float16* scales = reinterpret_cast<const _Float16*>(W + scale_off);
 
     // X loader: row tid/2, 32 halves starting at (tid%2)*32 of the K step.
@@ -80,7 +79,12 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(const uint8_t* __re
     const int wr = tid / 2;
     const int wb = tid % 2;
     const bool w_ok = n0 + wr < N;
-    const size_t wunit = size_t(w_ok ? n0 + wr : 0) * size_t(nb) + wb;
+    // Tiled layout: unit u of this row sits at code0 + u * ustride bytes and
+    // its scale at scale0 + u * (ustride / 16).
+    const TiledPos wpos = tiled_pos(kQ4_0, N, nb, w_ok ? n0 + wr : 0, wb);
+    const uint8_t* wcode = W + wpos.code;
+    const _Float16* wscale = scales + wpos.scale;
+    const uint32_t ustride = wpos.part_stride;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -103,8 +107,9 @@ __global__ __launch_bounds__(kThreads) void gemm_q4_0_kernel(const uint8_t* __re
             for (int v = 0; v < 4; ++v) xv[v] = u32x4{0u, 0u, 0u, 0u};
         }
         if (w_ok && k0 + wb * 32 < K) {   // K is a multiple of 32, not always of 64
-            cv = codes[wunit + k0 / 32];
-            d = scales[wunit + k0 / 32];
+            const uint32_t ku = uint32_t(k0 / 32);
+            cv = *reinterpret_cast<const u32x4*>(wcode + size_t(ku) * ustride);
+            d = wscale[size_t(ku) * (ustride / 16)];
         } else {
             cv = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
             d = (_Float16)0.0f;

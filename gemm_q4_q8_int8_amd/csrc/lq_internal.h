@@ -12,89 +12,96 @@ namespace lq {
 enum Fmt : int { kQ4_0 = 0, kQ8_0 = 1, kI8B64 = 2 };
 enum XType : int { kF32 = 0, kF16 = 1 };
 
-// Code bytes per 32-weight unit and scale bytes per scale.
-constexpr int unit_code_bytes(int fmt) { return fmt == kQ4_0 ? 16 : 32; }
+// ------------------------------------------------------ packed layout ----
+// Rows are grouped in tiles of 64.  A "unit" is one scale block of a row
+// (32 weights for Q4_0 / Q8_0, 64 for int8 block-64) and its codes are cut
+// into 16-byte parts (1, 2 or 4).  Inside a tile the codes are stored
+// unit-major, then part, then row: the 64 rows' copies of one part of one
+// unit are one contiguous 1 KB run, so one wave whose lane r owns row r of
+// the tile reads it with a single coalesced 16-byte-per-lane load.  The last
+// tile of a matrix may hold fewer than 64 rows (nr); its runs are nr * 16
+// bytes and nothing is padded.  The scale plane is laid out the same way with
+// one 2- or 4-byte scale in place of a 16-byte part.
+constexpr int kTileRows = 64;
+__host__ __device__ constexpr int unit_elems(int fmt) { return fmt == kI8B64 ? 64 : 32; }
+__host__ __device__ constexpr int unit_parts(int fmt) { return fmt == kQ4_0 ? 1 : (fmt == kQ8_0 ? 2 : 4); }
+__host__ __device__ constexpr int unit_bytes(int fmt) { return 16 * unit_parts(fmt); }
+__host__ __device__ constexpr int scale_bytes(int fmt) { return fmt == kI8B64 ? 4 : 2; }
 
-// Packed-layout geometry (the layout documented in lq.h).
 inline size_t code_plane_bytes(int fmt, int64_t N, int64_t K) {
     return fmt == kQ4_0 ? size_t(N) * size_t(K) / 2 : size_t(N) * size_t(K);
 }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline size_t scale_plane_bytes(int fmt, int64_t N, int64_t K) {
-    return fmt == kI8B64 ? size_t(N) * size_t(K / 64) * 4 : size_t(N) * size_t(K / 32) * 2;
+    return size_t(N) * size_t(K / unit_elems(fmt)) * size_t(scale_bytes(fmt));
+}
+
+// Position of (row, unit) in the tiled layout: `code` is the byte offset of
+// part 0 (part p adds p * nr * 16), `scale` the index of the unit's scale.
+struct TiledPos {
+    size_t code;
+    size_t scale;
+    uint32_t part_stride;   // nr * 16
+};
+__host__ __device__ inline TiledPos tiled_pos(int fmt, int64_t N, int64_t nu, int64_t row, int64_t u) {
+    const int64_t tile = row / kTileRows;
+    const int64_t r = row - tile * kTileRows;
+    const int64_t rest = N - tile * kTileRows;
+    const int64_t nr = rest < kTileRows ? rest : kTileRows;
+    const int64_t first = tile * kTileRows * nu;   // units stored before this tile
+    TiledPos p;
+    p.code = size_t(first + u * nr) * size_t(unit_bytes(fmt)) + size_t(r) * 16;
+    p.scale = size_t(first + u * nr + r);
+    p.part_stride = uint32_t(nr * 16);
+    return p;
 }
 
 // ---------------------------------------------------------------- GEMV ----
 constexpr int kMaxBatch = 16;       // descriptors per grouped launch
-constexpr int kGemvThreads = 256;
-// Rows per team per step: 8 for Q4_0 (16-byte units), 4 for the 32-byte int8
-// units, so two steps of code registers fit without spilling.
-#ifndef LQ_GEMV_RPI_Q4
-#define LQ_GEMV_RPI_Q4 8
-#endif
-#ifndef LQ_GEMV_RPI_I8
-#define LQ_GEMV_RPI_I8 4
-#endif
-// Steps of weight loads kept in flight per wave (register ring depth - 1).
-#ifndef LQ_GEMV_NBUF
-#define LQ_GEMV_NBUF 2
-#endif
-// Resident GEMV workgroups per CU (persistent grid size = CUs x this).
+constexpr int kGemvThreads = 256;   // 4 waves: one tile, K split four ways
+// Split-K scratch held by the library on every device (static device arrays):
+// partial sums of the K slices of a tile, and one arrival counter per tile.
+constexpr int64_t kGemvPartFloats = int64_t(1) << 20;   // 4 MiB
+constexpr int64_t kGemvCounters = int64_t(1) << 16;
+// Workgroups a launch aims for per CU before it splits K across workgroups,
+// and the fewest units a wave keeps when K is split.
 #ifndef LQ_GEMV_WGS_PER_CU
-#define LQ_GEMV_WGS_PER_CU 2
+#define LQ_GEMV_WGS_PER_CU 8
 #endif
-constexpr int gemv_rpi(int fmt) { return fmt == kQ4_0 ? LQ_GEMV_RPI_Q4 : LQ_GEMV_RPI_I8; }
-constexpr int kGemvXLdsFloats = 16384;   // LDS budget (floats) for a launch's activations
+#ifndef LQ_GEMV_MIN_UNITS
+#define LQ_GEMV_MIN_UNITS 4
+#endif
 
 struct GemvDesc {
-    const uint8_t* codes;   // code plane
-    const void* scales;     // scale plane (fp16 or fp32)
-    const void* x;          // activations in global memory (fp32 or fp16)
-    float* y;               // output rows
+    const uint8_t* codes;   // code plane (tiled)
+    const uint8_t* scales;  // scale plane (tiled)
+    const void* x;          // activations (fp32 or fp16), K values
+    float* y;               // N outputs
+    float* part;            // split-K partials: S slices x tiles * 64 floats (S > 1 only)
+    uint32_t* cnt;          // one arrival counter per tile (S > 1 only)
     int32_t N;              // rows
-    int32_t nu;             // 32-weight units per row (K / 32)
-    int32_t xdt;            // kF32 / kF16
-    int32_t nchunks;        // chunks of TP units per row
-    int32_t iters;          // row iterations (rows_per_iter rows each)
-    int32_t iter0;          // first row iteration of this matrix in the launch
-    int32_t x_off;          // LDS offset (floats) of its staged activations
+    int32_t nu;             // units per row (K / unit_elems)
+    int32_t tiles;          // ceil(N / 64)
+    int32_t S;              // K slices (workgroups per tile)
+    int32_t wg0;            // first workgroup of this matrix in the launch
     int32_t pad;
 };
 
-// One activation vector staged in LDS at the start of a launch.
-struct GemvXSrc {
-    const void* x;
-    int32_t K;
-    int32_t xdt;
-    int32_t lds_off;        // floats, a multiple of 32
-    int32_t pad;
-};
-
-struct GemvBatchArgs {
+struct GemvArgs {
     GemvDesc d[kMaxBatch];
-    GemvXSrc xs[kMaxBatch];
-    int32_t nx;             // activation vectors to stage
-    int32_t total_iters;
     int32_t count;
-    int32_t pad;
+    int32_t total_wgs;
 };
 
-// A team of `tp` lanes owns one row at a time; lane t of a team handles unit
-// t of each chunk of tp units.
-struct GemvConfig {
-    int tp;
-    int rpi;
-    int rows_per_iter;   // rows one workgroup covers per step
-    bool x_global;       // activations read from global memory (K too long for LDS)
-};
-
-GemvConfig gemv_config(int fmt, int nu);
-hipError_t launch_gemv(int fmt, const GemvConfig& cfg, const GemvBatchArgs& args,
-                       int grid, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_gemv(int fmt, int xdt, const GemvArgs& args, hipStream_t stream);
+// Device addresses of this device's split-K scratch (looked up once per device).
+hipError_t gemv_scratch(float** part, uint32_t** cnt);
 
 // ------------------------------------------------------- conversions ----
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,
                               hipStream_t stream);
+hipError_t launch_pack_planes(int fmt, const void* codes, const void* scales, void* dst, int64_t N,
+                              int64_t K, hipStream_t stream);
 hipError_t launch_dequant(int fmt, bool to_f16, const void* W, void* out, int64_t N,
                           int64_t K, hipStream_t stream);
 

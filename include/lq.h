@@ -27,28 +27,38 @@
  * which the "oxinfer" page stores quantized matrices ("Pre-quantized
  * checkpoints": codes and scales as separate tensors, in the kernels'
  * in-memory layout), a packed matrix is a code plane followed by a scale
- * plane.  With nb = K / block blocks per row and b = n * nb + (block index):
- *   LQ_Q4_0   codes: 16 bytes per block at offset 16 * b, GGUF byte order;
- *             scales: fp16 at offset lq_scale_offset() + 2 * b.
- *   LQ_Q8_0   codes: 32 int8 per block at offset 32 * b;
- *             scales: fp16 at offset lq_scale_offset() + 2 * b.
- *   LQ_I8B64  codes: int8, row-major N x K, at offset n * K + k;
- *             scales: fp32 at offset lq_scale_offset() + 4 * (n * K / 64 + k / 64).
- *   lq_scale_offset() is the code-plane size rounded up to 256 bytes.  The
+ * plane, both in the order the GPU kernels read them.
+ *   A unit is one scale block of one row: 32 weights (LQ_Q4_0, LQ_Q8_0) or 64
+ *   (LQ_I8B64), with nu = K / (unit weights) units per row.  Its codes are
+ *   P parts of 16 bytes: P = 1 (Q4_0: 16 bytes in GGUF byte order), 2 (Q8_0:
+ *   32 int8) or 4 (LQ_I8B64: 64 int8); part p holds the unit's code bytes
+ *   16p .. 16p + 15.  Its scale is fp16 (Q4_0, Q8_0) or fp32 (LQ_I8B64).
+ *   Rows are grouped in tiles of 64: tile t holds rows 64t .. 64t + nr - 1
+ *   with nr = min(64, N - 64t).  For row n = 64t + r and unit u:
+ *     code part p at byte   16 * (64 t nu P + (u P + p) nr + r)
+ *     scale at element      64 t nu + u nr + r   of the scale plane
+ *   (inside a tile: unit-major, then part, then row), so part p of unit u
+ *   for all rows of a tile is one contiguous run of nr * 16 bytes.  The
+ *   code plane is N K / 2 bytes (Q4_0) or N K bytes; the scale plane starts
+ *   at lq_scale_offset(), the code-plane size rounded up to 256 bytes.  The
  *   weight bytes equal those of the GGUF form (18 or 34 bytes per 32
- *   weights; 68 bytes per 64 for LQ_I8B64) plus at most 255 bytes of padding.
+ *   weights; 68 bytes per 64 for LQ_I8B64) plus at most 255 bytes of
+ *   padding between the planes (left as allocated).
  *
  * Conventions for every call.
  *   - Pointers named W, x, X, y, Y, out, dst, src, codes, scales, ws are
  *     DEVICE pointers (memory the caller allocated on the current HIP device);
  *     `descs` of lq_gemv_batch is a HOST pointer.  The caller owns every
  *     buffer; the library keeps no pointer after a call returns and allocates
- *     no device memory.
+ *     no device memory.  It holds one static scratch area per device (4 MiB
+ *     of partial sums and 256 KiB of counters, part of the loaded code
+ *     object) that lq_gemv / lq_gemv_batch use when they split K across
+ *     workgroups.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Calls only enqueue work (no implicit synchronisation); results are
  *     ready when the stream reaches that point.
- *   - Sizes are int64_t: N, K, M >= 1; N <= 2^31 - 1, M <= 2^31 - 1.  K must be
- *     a multiple of the format's block (32, 32, 64).
+ *   - Sizes are int64_t: N, K, M >= 1; N <= 2^31 - 1, M <= 2^31 - 1,
+ *     K <= 2^25.  K must be a multiple of the format's block (32, 32, 64).
  *   - Alignment: W, x, X, dst, out and codes must be 16-byte aligned; y, Y
  *     and scales 4-byte aligned; src (GGUF bytes) 2-byte aligned.
  *   - Activations: x / X are fp32 (LQ_F32) or fp16 (LQ_F16), contiguous; X is
@@ -59,7 +69,10 @@
  *     failure lq_last_error() returns a message for the calling thread.
  *     Nothing aborts, prints or throws across the ABI.
  *   - Thread safety: calls may come from several host threads; calls that
- *     write the same buffers must be ordered by the caller.
+ *     write the same buffers must be ordered by the caller.  GEMV calls on
+ *     one device share that device's split-K scratch: GEMV work enqueued on
+ *     different streams must not run at the same time (order the streams
+ *     with events); GEMV calls on one stream are always safe.
  */
 #ifndef LQ_H
 #define LQ_H
@@ -71,7 +84,7 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 1
+#define LQ_ABI_VERSION 2
 
 typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2 } lq_fmt;
 typedef enum lq_dtype { LQ_F32 = 0, LQ_F16 = 1 } lq_dtype;
@@ -118,11 +131,12 @@ size_t lq_gguf_bytes(int32_t fmt, int64_t N, int64_t K);
 lq_status lq_repack_gguf(int32_t fmt, const void* src, void* dst,
                          int64_t N, int64_t K, void* stream);
 
-/* Separate code and scale planes -> packed layout (two device copies).
- * codes: the code plane exactly as described above (N*nb*16 bytes for Q4_0,
- * N*K bytes for Q8_0 and LQ_I8B64); scales: N*nb fp16 (Q4_0, Q8_0) or
- * N*K/64 fp32 (LQ_I8B64).  This is the "oxinfer" page's split form
- * ("Pre-quantized checkpoints": X.q4 + X.q4s, X.q8 + X.q8s). */
+/* Row-major code and scale planes -> packed layout (a byte permutation).
+ * codes: the units' code bytes row by row, unit by unit (N * K / 2 bytes for
+ * Q4_0 in GGUF byte order, N * K int8 for Q8_0 and LQ_I8B64); scales: one
+ * per unit in the same order, N * K / 32 fp16 (Q4_0, Q8_0) or N * K / 64
+ * fp32 (LQ_I8B64).  This is the "oxinfer" page's split form ("Pre-quantized
+ * checkpoints": X.q4 + X.q4s, X.q8 + X.q8s). */
 lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales,
                          void* dst, int64_t N, int64_t K, void* stream);
 

@@ -20,6 +20,33 @@ def upload(fmt: str, w, scales, N, K):
     return upload_gguf(FMT[fmt], w, N, K)
 
 
+def tiled_reference(fmt: str, codes_rows: np.ndarray, scales_rows: np.ndarray, N, K) -> np.ndarray:
+    """Host construction of the packed layout that lq.h documents, from
+    row-major planes: codes_rows (N, units, unit bytes) uint8, scales_rows
+    (N, units) fp16 bits or fp32.  Rows go in tiles of 64 (the last may be
+    shorter); inside a tile, unit by unit, 16-byte part by part, the rows'
+    parts side by side; scales the same way, one per unit and row."""
+    E = 64 if fmt == "i8b64" else 32
+    P = {"q4_0": 1, "q8_0": 2, "i8b64": 4}[fmt]
+    nu = K // E
+    out = np.zeros(lq.lq_packed_bytes(FMT[fmt], N, K), np.uint8)
+    soff = lq.lq_scale_offset(FMT[fmt], N, K)
+    codes_rows = np.ascontiguousarray(codes_rows).view(np.uint8).reshape(N, nu, P, 16)
+    sc = np.ascontiguousarray(scales_rows).reshape(N, nu)
+    sbytes = sc.dtype.itemsize
+    cpos, spos = 0, soff
+    for t0 in range(0, N, 64):
+        nr = min(64, N - t0)
+        blk = np.ascontiguousarray(codes_rows[t0:t0 + nr].transpose(1, 2, 0, 3)).reshape(-1)
+        out[cpos:cpos + blk.size] = blk
+        cpos += blk.size
+        sb = np.ascontiguousarray(sc[t0:t0 + nr].T).view(np.uint8).reshape(-1)
+        out[spos:spos + sb.size] = sb
+        spos += sb.size
+    assert cpos == (N * K // 2 if fmt == "q4_0" else N * K) and spos == out.size
+    return out
+
+
 def guarded(n, dtype=torch.float32):
     buf = torch.full((n + GUARD,), SENTINEL, dtype=dtype, device="cuda")
     return buf

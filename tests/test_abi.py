@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 1
+    assert lq.lq_abi_version() == 2
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -71,6 +71,7 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_gemv(0, A16, A16, 0, A16, -3, 32, None) == SHAPE
     assert g.lq_gemv(0, A16, A16, 0, A16, 4, 48, None) == SHAPE
     assert g.lq_gemv(2, A16, A16, 0, A16, 4, 96, None) == SHAPE       # int8 block 64
+    assert g.lq_gemv(0, A16, A16, 0, A16, 4, 2**25 + 32, None) == SHAPE   # K above 2^25
     assert g.lq_gemv(0, A16, A16, 0, A16, 2 ** 31, 32, None) == SHAPE
     assert g.lq_gemv(0, None, A16, 0, A16, 4, 32, None) == ARG
     assert g.lq_gemv(0, A16 + 8, A16, 0, A16, 4, 32, None) == ALIGN

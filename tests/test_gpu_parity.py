@@ -16,7 +16,7 @@ import torch
 
 import gemm_q4_q8_int8_amd as lq
 import lqgen
-from gemm_q4_q8_int8_amd.device import to_device
+from gemm_q4_q8_int8_amd.device import to_device, upload_planes
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -109,20 +109,34 @@ def test_dequant_golden_blocks(oracle):
             assert y[0] == np.float32(float(blk["sum"])), blk["id"]
 
 
-def test_repack_roundtrip_planes():
-    """GGUF -> packed by lq_repack_gguf equals the plane layout built on the host."""
-    for fmt in ("q4_0", "q8_0"):
-        N, K = 9, 224
-        say("repack layout", fmt)
-        w, _ = make(fmt, 77, N, K)
-        Wd = gu.upload(fmt, w, None, N, K)
-        packed = Wd.cpu().numpy()
-        bb = 18 if fmt == "q4_0" else 34
-        blk = w.reshape(-1, bb)
-        code_plane = blk[:, 2:].reshape(-1)
+@pytest.mark.parametrize("N", [9, 64, 130])
+def test_repack_roundtrip_planes(N):
+    """lq_repack_gguf and lq_pack_planes both produce the documented tiled
+    layout, byte for byte, as built on the host from the same blocks."""
+    for fmt in ("q4_0", "q8_0", "i8b64"):
+        K = 128 if fmt == "i8b64" else 224
+        say("packed layout", fmt, N, K)
+        w, s = make(fmt, 77 + N, N, K)
+        if fmt == "i8b64":
+            codes = w.reshape(N, K // 64, 64)
+            scales = s.reshape(N, K // 64)
+        else:
+            bb = 18 if fmt == "q4_0" else 34
+            blk = w.view(np.uint8).reshape(N, K // 32, bb)
+            codes = np.ascontiguousarray(blk[:, :, 2:])
+            scales = np.ascontiguousarray(blk[:, :, 0:2]).view(np.uint16).reshape(N, K // 32)
+        want = gu.tiled_reference(fmt, codes, scales, N, K)
+        cb = N * K // 2 if fmt == "q4_0" else N * K
         off = lq.lq_scale_offset(gu.FMT[fmt], N, K)
-        assert np.array_equal(packed[:code_plane.size], code_plane)
-        assert np.array_equal(packed[off:off + 2 * blk.shape[0]], blk[:, 0:2].reshape(-1))
+        got = [("pack_planes", upload_planes(gu.FMT[fmt], codes.reshape(-1), scales.reshape(-1), N, K))]
+        if fmt != "i8b64":
+            got.append(("repack_gguf", gu.upload(fmt, w, None, N, K)))
+        for name, Wd in got:
+            b = Wd.cpu().numpy()
+            assert b.size == want.size, name
+            # the bytes between the planes are padding and left as allocated
+            assert np.array_equal(b[:cb], want[:cb]), name + " codes"
+            assert np.array_equal(b[off:], want[off:]), name + " scales"
 
 
 # ---------------------------------------------------------------- GEMV ----
