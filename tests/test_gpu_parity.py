@@ -303,8 +303,11 @@ def test_workload_i8b64_layers(oracle):
 
 # ---------------------------------------------------------------- GEMM ----
 
+# Covers row, column and K tails, odd block counts, and K split across
+# workgroups (2 or 4 slices, uneven last slice).
 GEMM_SHAPES = [(16, 64, 64), (5, 33, 96), (130, 129, 160), (1, 128, 64), (200, 300, 2048),
-               (512, 256, 1024), (64, 2048, 1376)]
+               (512, 256, 1024), (64, 2048, 1376), (96, 200, 1120), (300, 130, 1056),
+               (257, 385, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
