@@ -213,7 +213,7 @@ __device__ __forceinline__ float unit_fma(const Unit<FMT>& b, const void* xv, in
 // Units whose loads one wave issues before computing (register budget: the
 // codes of UNR units stay live).
 template <int FMT>
-constexpr int unroll_of() { return FMT == kQ4_0 ? 8 : (FMT == kQ8_0 ? 4 : 2); }
+constexpr int unroll_of() { return FMT == kQ4_0 ? LQ_GEMV_UNR_Q4 : (FMT == kQ8_0 ? LQ_GEMV_UNR_Q8 : LQ_GEMV_UNR_I8); }
 
 // sum_{j < S} p[j * pitch] in slice order, loads issued eight at a time so
 // their latencies overlap.

@@ -68,6 +68,16 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #ifndef LQ_GEMV_WGS_PER_CU
 #define LQ_GEMV_WGS_PER_CU 8
 #endif
+// Units whose loads one wave issues before computing them (per format).
+#ifndef LQ_GEMV_UNR_Q4
+#define LQ_GEMV_UNR_Q4 8
+#endif
+#ifndef LQ_GEMV_UNR_Q8
+#define LQ_GEMV_UNR_Q8 4
+#endif
+#ifndef LQ_GEMV_UNR_I8
+#define LQ_GEMV_UNR_I8 2
+#endif
 #ifndef LQ_GEMV_MIN_UNITS
 #define LQ_GEMV_MIN_UNITS 4
 #endif
