@@ -193,6 +193,59 @@ def test_gemv_batch_mixed(oracle):
         assert gu.ratio(y[:N].cpu().numpy(), yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, (fmt, N, K)
 
 
+def test_graph_replays_match_eager(oracle):
+    """GEMV launches that split K (per-device counters and partials), a
+    grouped launch and a split-K GEMM (workspace + ordered reduction),
+    captured in one graph and replayed several times with eager work of the
+    same kernels in between: every replay equals the eager result bit for
+    bit, and the eager result passes the oracle."""
+    say("graph replays")
+    gemv_cases = [("q8_0", 96, 4096, np.float32), ("i8b64", 300, 2048, np.float16), ("q4_0", 64, 896, np.float32)]
+    descs, ref_data = [], []
+    for i, (fmt, N, K, xdt) in enumerate(gemv_cases):
+        w, s = make(fmt, 3100 + i, N, K)
+        x = lqgen.activations(3200 + i, K, xdt)
+        descs.append((gu.FMT[fmt], gu.upload(fmt, w, s, N, K), to_device(x), torch.zeros(N, device="cuda"), N, K))
+        ref_data.append((fmt, w, s, x, N, K))
+    M, Ng, Kg = 96, 200, 1024
+    wg, _ = make("q4_0", 3300, Ng, Kg)
+    Wg = gu.upload("q4_0", wg, None, Ng, Kg)
+    Xg = to_device(lqgen.activations(3301, M * Kg, np.float16).reshape(M, Kg))
+    Yg = torch.zeros(M * Ng, device="cuda")
+    wsb = lq.lq_gemm_workspace_bytes(lq.LQ_Q4_0, M, Ng, Kg)
+    assert wsb > 0, "shape meant to split K"
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def run():
+        lq.lq_gemv_batch([descs[0]])
+        lq.lq_gemv_batch(descs[1:])
+        lq.lq_gemm(lq.LQ_Q4_0, Wg, Xg, Yg, M, Ng, Kg, ws=ws, ws_bytes=wsb)
+
+    outs = [d[3] for d in descs] + [Yg]
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for (fmt, w, s, x, N, K), y in zip(ref_data, eager):
+        yr, S = oracle.gemv(ORACLE_FMT[fmt], w, s, x, N, K)
+        assert gu.ratio(y.cpu().numpy(), yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, fmt
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs from the eager result"
+        run()                       # eager work of the same kernels between replays
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"eager run after replay {rep} differs"
+
+
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
 def test_gemv_invariants(oracle, fmt):
     N, K = 96, 2048 if fmt != "q4_0" else 896
