@@ -22,7 +22,8 @@ FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64}
 # Every symbol include/lq.h declares.
 EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq_scale_offset",
            "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_dequant_f32",
-           "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemm_workspace_bytes", "lq_gemm",
+           "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi", "lq_gemm_workspace_bytes",
+           "lq_gemm",
            "lq_matmul", "lq_status_str", "lq_last_error")
 
 
@@ -69,6 +70,7 @@ def load(path: str = LIB_PATH):
         "lq_dequant_f16": ([i32, vp, vp, i64, i64, vp], i32),
         "lq_gemv": ([i32, vp, vp, i32, vp, i64, i64, vp], i32),
         "lq_gemv_batch": ([ctypes.POINTER(lq_gemv_desc), i32, vp], i32),
+        "lq_gemv_multi": ([i32, vp, vp, i32, vp, i64, i64, i64, vp], i32),
         "lq_gemm_workspace_bytes": ([i32, i64, i64, i64], sz),
         "lq_gemm": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_matmul": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
@@ -188,6 +190,12 @@ def lq_gemv_batch(descs, stream=None):
     for i, (fmt, W, x, y, N, K) in enumerate(descs):
         arr[i] = lq_gemv_desc(_fmt(fmt), _xdt(x), _ptr(W), _ptr(x), _ptr(y), N, K)
     _check(load().lq_gemv_batch(arr, len(descs), _stream(stream)))
+
+
+def lq_gemv_multi(fmt, W, X, Y, M, N, K, stream=None, xdt=None):
+    xdt = _xdt(X) if xdt is None else xdt
+    _check(load().lq_gemv_multi(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K,
+                                _stream(stream)))
 
 
 def lq_gemm(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=0, stream=None, xdt=None):

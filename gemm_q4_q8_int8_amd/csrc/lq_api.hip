@@ -274,6 +274,49 @@ lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt, float*
     return lq_gemv_batch(&d, 1, stream);
 }
 
+lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
+                        int64_t N, int64_t K, void* stream) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    LQ_TRY(check_xdt(xdt));
+    if (xdt != LQ_F16) return fail(LQ_ERR_UNSUPPORTED, "lq_gemv_multi takes LQ_F16 activations");
+    if (M < 1 || M > lq::kMultiMaxTokens)
+        return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, %d]", (long long)M, lq::kMultiMaxTokens);
+    LQ_TRY(check_ptr(W, 16, "W"));
+    LQ_TRY(check_ptr(X, 16, "X"));
+    LQ_TRY(check_ptr(Y, 4, "Y"));
+    int cus = 0;
+    LQ_TRY(device_cus(&cus));
+    const int64_t tiles = (N + lq::kTileRows - 1) / lq::kTileRows;
+    const int64_t nu = K / lq::unit_elems(fmt);
+    // K split as for the single-token GEMV, bounded by the scratch area.
+    int64_t S = 1;
+    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
+    if (tiles < target) {
+        S = std::min((target + tiles - 1) / tiles, std::max<int64_t>(1, nu / (4 * LQ_GEMV_MIN_UNITS)));
+        S = std::min(S, std::max<int64_t>(1, lq::kGemvPartFloats / (M * tiles * lq::kTileRows)));
+        if (tiles > lq::kGemvCounters) S = 1;
+    }
+    if (tiles * S > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows");
+    lq::MultiDesc d = {};
+    d.codes = static_cast<const uint8_t*>(W);
+    d.scales = static_cast<const uint8_t*>(W) + lq::align256(lq::code_plane_bytes(fmt, N, K));
+    d.x = static_cast<const _Float16*>(X);
+    d.y = Y;
+    d.N = int32_t(N);
+    d.K = int32_t(K);
+    d.nu = int32_t(nu);
+    d.tiles = int32_t(tiles);
+    d.S = int32_t(S);
+    d.M = int32_t(M);
+    d.vec_y = (aligned(Y, 16) && N % 4 == 0) ? 1 : 0;
+    if (S > 1) {
+        const hipError_t e = lq::gemv_scratch(&d.part, &d.cnt);
+        if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
+    }
+    const hipError_t e = lq::launch_gemv_multi(fmt, d, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "multi-token GEMV launch");
+}
+
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
     if (check_fmt_shape(fmt, N, K) != LQ_OK || M < 1) return 0;
     return lq::gemm_workspace_bytes(M, N, K);
@@ -303,6 +346,8 @@ lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt, float*
 lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
                     int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
     if (M == 1) return lq_gemv(fmt, W, X, xdt, Y, N, K, stream);
+    if (M <= lq::kMultiMaxTokens && xdt == LQ_F16)
+        return lq_gemv_multi(fmt, W, X, xdt, Y, M, N, K, stream);
     return lq_gemm(fmt, W, X, xdt, Y, M, N, K, ws, ws_bytes, stream);
 }
 

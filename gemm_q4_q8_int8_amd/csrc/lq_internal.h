@@ -107,6 +107,38 @@ hipError_t launch_gemv(int fmt, int xdt, const GemvArgs& args, hipStream_t strea
 // Device addresses of this device's split-K scratch (looked up once per device).
 hipError_t gemv_scratch(float** part, uint32_t** cnt);
 
+// ------------------------------------------------- multi-token GEMV ----
+constexpr int kMultiMaxTokens = 16;   // tokens of one MFMA fragment
+// Units whose loads one wave issues before computing them (per format).
+#ifndef LQ_MULTI_UNR_Q4
+#define LQ_MULTI_UNR_Q4 8
+#endif
+#ifndef LQ_MULTI_UNR_Q8
+#define LQ_MULTI_UNR_Q8 4
+#endif
+#ifndef LQ_MULTI_UNR_I8
+#define LQ_MULTI_UNR_I8 2
+#endif
+
+struct MultiDesc {
+    const uint8_t* codes;   // code plane (tiled)
+    const uint8_t* scales;  // scale plane (tiled)
+    const _Float16* x;      // M x K activations, row-major
+    float* y;               // M x N outputs, row-major
+    float* part;            // split-K partials: S slices x M tokens x tiles * 64 floats (S > 1 only)
+    uint32_t* cnt;          // one arrival counter per tile (S > 1 only)
+    int32_t N;              // rows (and the row pitch of y)
+    int32_t K;              // reduction length (and the row pitch of x)
+    int32_t nu;             // units per row
+    int32_t tiles;          // ceil(N / 64)
+    int32_t S;              // K slices (workgroups per tile)
+    int32_t M;              // tokens, 1 .. kMultiMaxTokens
+    int32_t vec_y;          // y rows are 16-byte aligned: full tiles store float4
+    int32_t pad;
+};
+
+hipError_t launch_gemv_multi(int fmt, const MultiDesc& d, hipStream_t stream);
+
 // ------------------------------------------------------- conversions ----
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,
                               hipStream_t stream);

@@ -1,0 +1,321 @@
+// Multi-token GEMV: Y[t, n] = sum_k w[n, k] X[t, k] for t < M <= 16 tokens,
+// fp16 activations, weights in the tiled packed layout (Q4_0 / Q8_0 / int8
+// block-64).  This is the decode step of a few tokens at once, as when a
+// drafted run of tokens is verified in one pass ("oxinfer" page, "Speculative
+// decoding"; "How it works", the multi-token variants of the decode kernels).
+//
+// The weights are still read once, so the step stays bound by HBM bandwidth
+// for any M <= 16, while the arithmetic grows M-fold.  Per-lane FMAs would
+// make it instruction-bound (the page observes exactly that for its Q4
+// multi-token kernels), so the products run on the matrix cores:
+//   * One v_mfma_f32_16x16x32_f16 per (16 rows, one 32-element block): A is
+//     the 16 x 32 activation fragment (row = token), B the 32 x 16 weight
+//     fragment (column = weight row) holding the EXACT integer codes (q - 8
+//     or c) as fp16.  Products are exact and the block sum is fp32, so the
+//     block scale is applied afterwards by an fp32 FMA: no weight is rounded
+//     to fp16, and the result meets the GEMV accuracy bound, not the looser
+//     one of the fp16-tile GEMM.
+//   * A workgroup of 4 waves takes one 64-row tile and splits its units four
+//     ways (and K across workgroups when the matrix has few tiles), like the
+//     single-token GEMV, with the same split-K scratch.
+//   * Lane (r, g) (r = lane % 16, g = lane / 16) loads tile row 4r + g of a
+//     unit with one 16-byte load: the wave's load is the unit's contiguous
+//     1 KB run.  Four cross-row swaps (v_permlane32_swap, v_permlane16_swap)
+//     transpose the 4 x 4 dwords of lanes r, r+16, r+32, r+48, after which
+//     lane (r, j) holds dword j of rows 4r, 4r+1, 4r+2, 4r+3: the B fragment
+//     of row group m (weight rows 4r + m as column r) for k-set j.
+//   * The MFMA output lane (r, j) then holds tokens 4j..4j+3 of weight rows
+//     4r + m, so the scales it needs are the four consecutive ones of rows
+//     4r..4r+3: one 8- or 16-byte load per unit.
+//   * The k order inside a block is free as long as A and B agree: lane
+//     group j takes elements 4j..4j+3 and 16+4j..16+4j+3, which for Q4_0 are
+//     exactly the low and high nibbles of code dword j.
+#include "lq_internal.h"
+
+namespace lq {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(orv));
+    return r;
+}
+
+// Transpose of the 4 x 4 dwords held by lanes r, r+16, r+32, r+48: on return
+// lane (r, j) holds in slot m what lane (r, m) held in slot j.
+__device__ __forceinline__ u32x4 xpose(const u32x4 c) {
+    const auto a = __builtin_amdgcn_permlane32_swap(c.x, c.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(c.y, c.w, false, false);
+    const auto lo = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// B fragment of Q4_0 code dword j (bytes 4j..4j+3 of a block) as 8 exact fp16
+// values q - 8, elements in the order 4j, 4j+2, 4j+1, 4j+3, 16+4j, 16+4j+2,
+// 16+4j+1, 16+4j+3.  A nibble at bits 0-3 of a half under exponent 0x6400 is
+// 1024 + q (minus 1032 gives q - 8); at bits 4-7 it is 1024 + 16 q, and
+// (1024 + 16 q) / 16 - 72 = q - 8 in one fused multiply-add.  Every step is
+// exact.
+__device__ __forceinline__ half8_t q4_frag(uint32_t d) {
+    const uint32_t kExp = 0x64006400u;
+    const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t e = d >> 8;
+    const half2_t a = as_h2(and_or(d, 0x000F000Fu, kExp)) - off;
+    const half2_t b = as_h2(and_or(e, 0x000F000Fu, kExp)) - off;
+    const half2_t c = __builtin_elementwise_fma(as_h2(and_or(d, 0x00F000F0u, kExp)), sixteenth, off_hi);
+    const half2_t f = __builtin_elementwise_fma(as_h2(and_or(e, 0x00F000F0u, kExp)), sixteenth, off_hi);
+    return __builtin_bit_cast(half8_t, u32x4{as_u32(a), as_u32(b), as_u32(c), as_u32(f)});
+}
+
+// B fragment of int8 codes: dword lo holds elements 4j..4j+3, dword hi the
+// elements 16 further on, in element order.  Flipping each sign bit gives
+// c + 128; a byte permute places two of those under 0x64 (fp16 1024 + v) and
+// subtracting 1152 leaves the exact codes.
+__device__ __forceinline__ half8_t i8_frag(uint32_t lo, uint32_t hi) {
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+    const half2_t p0 = as_h2(__builtin_amdgcn_perm(0x64646464u, a, 0x04010400u)) - off;
+    const half2_t p1 = as_h2(__builtin_amdgcn_perm(0x64646464u, a, 0x04030402u)) - off;
+    const half2_t p2 = as_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u)) - off;
+    const half2_t p3 = as_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)) - off;
+    return __builtin_bit_cast(half8_t, u32x4{as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)});
+}
+
+// A fragment (activations of one token) matching the B fragment's element
+// order: lo = x[4j .. 4j+3], hi = x[16+4j .. 16+4j+3] as fp16 pairs.
+template <int FMT>
+__device__ __forceinline__ half8_t x_frag(const u32x2 lo, const u32x2 hi) {
+    if constexpr (FMT == kQ4_0) {
+        // (x0, x2), (x1, x3) of each group of four.
+        return __builtin_bit_cast(
+            half8_t, u32x4{__builtin_amdgcn_perm(lo.y, lo.x, 0x05040100u),
+                           __builtin_amdgcn_perm(lo.y, lo.x, 0x07060302u),
+                           __builtin_amdgcn_perm(hi.y, hi.x, 0x05040100u),
+                           __builtin_amdgcn_perm(hi.y, hi.x, 0x07060302u)});
+    } else {
+        return __builtin_bit_cast(half8_t, u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+}
+
+// 32-element steps (MFMAs per row group) in one unit.
+template <int FMT>
+constexpr int steps_of() { return FMT == kI8B64 ? 2 : 1; }
+
+template <int FMT>
+constexpr int multi_unroll() {
+    return FMT == kQ4_0 ? LQ_MULTI_UNR_Q4 : (FMT == kQ8_0 ? LQ_MULTI_UNR_Q8 : LQ_MULTI_UNR_I8);
+}
+
+template <int FMT>
+struct MUnit {
+    static constexpr int P = unit_parts(FMT);
+    static constexpr int KS = steps_of<FMT>();
+    u32x4 c[P];          // codes of tile row 4r + g (this lane's load)
+    u32x2 xl[KS], xh[KS];  // activations of this lane's token and k-set
+    uint32_t s[4];       // raw scales of rows 4r .. 4r+3
+};
+
+// sum_{j < S} p[j * pitch] in slice order (eight loads in flight).
+__device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S) {
+    float t = 0.0f;
+    for (int j = 0; j < S; j += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = __hip_atomic_load(p + size_t(min(j + k, S - 1)) * pitch, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (j + k < S) t += v[k];
+    }
+    return t;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiDesc D) {
+    constexpr int P = unit_parts(FMT);
+    constexpr int UB = unit_bytes(FMT);
+    constexpr int SB = scale_bytes(FMT);
+    constexpr int E = unit_elems(FMT);
+    constexpr int KS = steps_of<FMT>();
+    constexpr int UNR = multi_unroll<FMT>();
+    __shared__ float red[4][16][64];
+    __shared__ uint32_t arrival;
+
+    const int N = D.N, nu = D.nu, S = D.S, M = D.M;
+    const int tile = int(blockIdx.x) / S;
+    const int slice = int(blockIdx.x) - tile * S;
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int lane = int(threadIdx.x) & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nr = min(kTileRows, N - tile * kTileRows);
+    const bool full = nr == kTileRows;
+
+    const int sa = int(int64_t(nu) * slice / S);
+    const int sb = int(int64_t(nu) * (slice + 1) / S);
+    const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / 4);
+    const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / 4);
+
+    const size_t first = size_t(tile) * kTileRows * size_t(nu);
+    const uint8_t* cbase = D.codes + first * UB;
+    const uint8_t* sbase = D.scales + first * SB;
+    // Rows past the end of a partial tile are re-read from the last row and
+    // never stored; so are tokens past M.
+    const uint32_t c_lane = uint32_t(min(4 * r + g, nr - 1)) * 16u;
+    const uint32_t c_unit = uint32_t(nr) * UB;
+    const uint32_t c_part = uint32_t(nr) * 16u;
+    const uint32_t s_unit = uint32_t(nr) * SB;
+    uint32_t s_row[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
+    const _Float16* xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + 4 * g;
+
+    f32x4 acc[4] = {};
+    for (int u = ua; u < ub; u += UNR) {
+        MUnit<FMT> b[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t uu = uint32_t(min(u + k, ub - 1));
+            const uint32_t co = uu * c_unit + c_lane;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                b[k].c[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(cbase + co + uint32_t(p) * c_part));
+            const uint8_t* sp = sbase + uu * s_unit;
+            if (full) {
+                if constexpr (SB == 2) {
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(sp + s_row[0]);
+                    b[k].s[0] = v.x & 0xFFFFu;
+                    b[k].s[1] = v.x >> 16;
+                    b[k].s[2] = v.y & 0xFFFFu;
+                    b[k].s[3] = v.y >> 16;
+                } else {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(sp + s_row[0]);
+                    b[k].s[0] = v.x;
+                    b[k].s[1] = v.y;
+                    b[k].s[2] = v.z;
+                    b[k].s[3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if constexpr (SB == 2) b[k].s[m] = *reinterpret_cast<const uint16_t*>(sp + s_row[m]);
+                    else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + s_row[m]);
+                }
+            }
+            const _Float16* xp = xrow + size_t(uu) * E;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                b[k].xl[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks);
+                b[k].xh[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks + 16);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            if (u + k >= ub) continue;
+            u32x4 t[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) t[p] = xpose(b[k].c[p]);
+            half8_t xa[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) xa[ks] = x_frag<FMT>(b[k].xl[ks], b[k].xh[ks]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    half8_t wb;
+                    if constexpr (FMT == kQ4_0) wb = q4_frag(t[0][m]);
+                    else wb = i8_frag(t[2 * ks][m], t[2 * ks + 1][m]);
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ks], wb, s, 0, 0, 0);
+                }
+                float d;
+                if constexpr (SB == 4) d = __uint_as_float(b[k].s[m]);
+                else d = (float)__builtin_bit_cast(_Float16, uint16_t(b[k].s[m]));
+                acc[m] = __builtin_elementwise_fma(f32x4{d, d, d, d}, s, acc[m]);
+            }
+        }
+    }
+
+    // Sum the four waves' K quarters; wave w then owns token 4g + w of rows
+    // 4r .. 4r+3.
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[w][4 * m + i][lane] = acc[m][i];
+    __syncthreads();
+    float v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        v[m] = (red[0][4 * m + w][lane] + red[1][4 * m + w][lane]) +
+               (red[2][4 * m + w][lane] + red[3][4 * m + w][lane]);
+    const int token = 4 * g + w;
+    const size_t row0 = size_t(tile) * kTileRows + size_t(4 * r);
+    if (S == 1) {
+        if (token < M) {
+            float* yp = D.y + size_t(token) * size_t(N) + row0;
+            if (D.vec_y && full) {
+                *reinterpret_cast<f32x4*>(yp) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (4 * r + m < nr) yp[m] = v[m];
+            }
+        }
+        return;
+    }
+    // Split K: publish this slice, then the last workgroup to arrive adds the
+    // slices in slice order.  Partials and counter are accessed only with
+    // device-scope atomics (see the single-token GEMV for why no fence).
+    const size_t pitch = size_t(D.tiles) * kTileRows;   // floats per token of one slice
+    const size_t spitch = pitch * size_t(M);             // floats per slice
+    if (token < M) {
+        float* pp = D.part + size_t(slice) * spitch + size_t(token) * pitch + row0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            __hip_atomic_store(pp + m, v[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        arrival = __hip_atomic_fetch_add(&D.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != uint32_t(S - 1)) return;
+    if (token < M) {
+        const float* pp = D.part + size_t(token) * pitch + row0;
+        float* yp = D.y + size_t(token) * size_t(N) + row0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float t = sum_slices(pp + m, spitch, S);
+            if (4 * r + m < nr) yp[m] = t;
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&D.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_multi(int fmt, const MultiDesc& d, hipStream_t stream) {
+    const dim3 grid(unsigned(d.tiles) * unsigned(d.S)), block(kGemvThreads);
+    switch (fmt) {
+        case kQ4_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ4_0>, grid, block, 0, stream, d); break;
+        case kQ8_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ8_0>, grid, block, 0, stream, d); break;
+        case kI8B64: hipLaunchKernelGGL(gemv_multi_kernel<kI8B64>, grid, block, 0, stream, d); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lq

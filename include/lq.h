@@ -52,8 +52,8 @@
  *     buffer; the library keeps no pointer after a call returns and allocates
  *     no device memory.  It holds one static scratch area per device (4 MiB
  *     of partial sums and 256 KiB of counters, part of the loaded code
- *     object) that lq_gemv / lq_gemv_batch use when they split K across
- *     workgroups.
+ *     object) that lq_gemv / lq_gemv_batch / lq_gemv_multi use when they
+ *     split K across workgroups.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Calls only enqueue work (no implicit synchronisation); results are
  *     ready when the stream reaches that point.
@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 2
+#define LQ_ABI_VERSION 3
 
 typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2 } lq_fmt;
 typedef enum lq_dtype { LQ_F32 = 0, LQ_F16 = 1 } lq_dtype;
@@ -175,6 +175,20 @@ typedef struct lq_gemv_desc {
  * descriptor is validated before anything is enqueued. */
 lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
 
+/* Multi-token GEMV, the decode step of a few tokens at once (verification of
+ * drafted tokens: "oxinfer" page, "Speculative decoding", and the multi-token
+ * variants of its decode kernels in "How it works"):
+ *   Y[m, n] = sum_k w[n,k] * X[m,k]   for m < M, n < N,
+ * every weight read once for all M tokens.  The weights are decoded exactly
+ * and multiplied on the matrix cores (fp16 x exact integer code, fp32 block
+ * sums), the block scale applied in fp32.  W: packed N x K; X: M x K fp16
+ * row-major (xdt must be LQ_F16, else LQ_ERR_UNSUPPORTED); Y: M x N fp32
+ * row-major.  1 <= M <= 16, else LQ_ERR_SHAPE.  Accuracy as lq_gemv, per
+ * output: |Y - Y_exact| <= 1e-4 * sum_k |w x| + 1e-6.  Shares the GEMV
+ * split-K scratch (see thread safety above). */
+lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt,
+                        float* Y, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Workspace bytes lq_gemm needs for these arguments (0 means none). */
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 
@@ -191,8 +205,9 @@ lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt,
 
 /* Route by token count, after the "oxinfer" page's rule that GPU matmul
  * kernels take only prompt-sized work ("Platforms and accelerators": t >= 16
- * tokens): M == 1 runs lq_gemv on X (fp32 or fp16); M >= 2 runs lq_gemm.
- * Arguments as in lq_gemm. */
+ * tokens): M == 1 runs lq_gemv on X (fp32 or fp16); 2 <= M <= 16 with fp16 X
+ * runs lq_gemv_multi; everything else runs lq_gemm.  Arguments as in
+ * lq_gemm. */
 lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt,
                     float* Y, int64_t M, int64_t N, int64_t K,
                     void* ws, size_t ws_bytes, void* stream);

@@ -238,3 +238,11 @@ def q4_0_prefill_ffn_2048x11008(M: int = 512) -> Workload:
     base = seed_of(4, 0, 15)
     xs = {"x_ffn": (base + 1, 2048, np.float16), "x_down": (base + 2, 11008, np.float16)}
     return Workload(f"q4_0_prefill_ffn_m{M}", mats, xs, M=M)
+
+
+def multi_token(wl: Workload, M: int) -> Workload:
+    """The same matrices decoded for M tokens at once (a verification pass
+    over M drafted tokens): every activation vector becomes an M x K fp16
+    N(0,1) matrix drawn from the same seed."""
+    xs = {k: (seed, n, np.float16) for k, (seed, n, _) in wl.xs.items()}
+    return Workload(f"{wl.name}_m{M}", list(wl.mats), xs, M=M)

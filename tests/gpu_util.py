@@ -82,3 +82,12 @@ def ratio(y, yref, S, rel, abs_):
     y = np.asarray(y, np.float64)
     assert np.all(np.isfinite(y)), "non-finite output"
     return float(np.max(np.abs(y - yref) / (rel * S + abs_))) if y.size else 0.0
+
+
+def gemv_multi(fmt: str, Wd, X: np.ndarray, M, N, K):
+    Xd = to_device(X)
+    Y = guarded(M * N)
+    lq.lq_gemv_multi(FMT[fmt], Wd, Xd, Y, M, N, K)
+    torch.cuda.synchronize()
+    check_guard(Y, M * N)
+    return Y[:M * N].cpu().numpy().reshape(M, N)

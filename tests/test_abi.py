@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 2
+    assert lq.lq_abi_version() == 3
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -93,6 +93,17 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_gemm(0, A16, A16 + 2, 1, A16, 16, 32, 32, None, 0, None) == ALIGN
     assert g.lq_gemm(0, A16, A16, 7, A16, 16, 32, 32, None, 0, None) == DTYPE
     assert g.lq_matmul(0, A16, A16, 1, A16, 0, 32, 32, None, 0, None) == SHAPE
+    # multi-token GEMV: fp16 activations, 1 <= M <= 16
+    assert g.lq_gemv_multi(0, A16, A16, 0, A16, 4, 64, 32, None) == UNSUP
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 0, 64, 32, None) == SHAPE
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 17, 64, 32, None) == SHAPE
+    assert g.lq_gemv_multi(2, A16, A16, 1, A16, 4, 64, 32, None) == SHAPE   # int8 block 64
+    assert g.lq_gemv_multi(9, A16, A16, 1, A16, 4, 64, 32, None) == FMT
+    assert g.lq_gemv_multi(0, A16, A16 + 8, 1, A16, 4, 64, 32, None) == ALIGN
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16 + 1, 4, 64, 32, None) == ALIGN
+    assert g.lq_gemv_multi(0, A16, None, 1, A16, 4, 64, 32, None) == ARG
+    assert g.lq_gemv_multi(0, A16, A16, 3, A16, 4, 64, 32, None) == DTYPE
+    assert g.lq_matmul(0, A16, A16, 1, A16, 4, 64, 48, None, 0, None) == SHAPE
     # conversions
     assert g.lq_repack_gguf(2, A16, A16, 4, 64, None) == FMT
     assert g.lq_repack_gguf(0, A16 + 1, A16, 4, 64, None) == ALIGN

@@ -1,0 +1,209 @@
+"""GPU parity of the multi-token GEMV (lq_gemv_multi) against the CPU oracle.
+
+Y[m, n] = sum_k w[n,k] X[m,k] for up to 16 tokens with fp16 activations.  The
+bar is the single-token GEMV's, per output: |Y - Y_ref| <= 1e-4 * sum|w x| +
+1e-6, since the weights are decoded exactly and only the fp32 sums round.
+Shapes span several 64-row tiles, partial last tiles, one-block rows, K split
+across workgroups, and every token count from 1 to 16.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_q4_q8_int8_amd as lq
+import lqgen
+from gemm_q4_q8_int8_amd.device import to_device
+from tests import gpu_util as gu
+from tests.test_gpu_parity import ORACLE_FMT, make, set_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    lq.load()
+    lq.lq_init()
+    yield
+
+
+# (fmt, M, N, K): tails in rows (N % 64) and tokens, single-block rows, long
+# K (split across workgroups when N is small), and big-N single-slice cases.
+MULTI_SHAPES = [
+    ("q4_0", 1, 1, 32), ("q4_0", 2, 5, 64), ("q4_0", 3, 67, 96), ("q4_0", 16, 64, 896),
+    ("q4_0", 5, 130, 960), ("q4_0", 8, 300, 2048), ("q4_0", 13, 33, 11008), ("q4_0", 16, 2500, 896),
+    ("q4_0", 4, 17, 25600),
+    ("q8_0", 1, 3, 32), ("q8_0", 2, 70, 512), ("q8_0", 7, 130, 2048), ("q8_0", 16, 64, 8192),
+    ("q8_0", 11, 200, 5632), ("q8_0", 16, 1100, 1024),
+    ("i8b64", 1, 1, 64), ("i8b64", 3, 77, 128), ("i8b64", 16, 256, 2048), ("i8b64", 6, 45, 5632),
+    ("i8b64", 16, 130, 8192), ("i8b64", 9, 5, 30720), ("i8b64", 14, 1500, 512),
+]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", MULTI_SHAPES)
+def test_multi_parity(oracle, fmt, M, N, K):
+    say("gemv_multi", fmt, M, N, K)
+    w, s = make(fmt, 2000 + N + K + M, N, K)
+    if N > 3:
+        w, s = set_scales(fmt, w, s, N, K, [2.0 ** -24, -0.75, 0.0, 3e-6])
+    X = lqgen.activations(6000 + M + K, M * K, np.float16).reshape(M, K)
+    Wd = gu.upload(fmt, w, s, N, K)
+    Y = gu.gemv_multi(fmt, Wd, X, M, N, K)
+    Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K)
+    r = gu.ratio(Y, Yr, S, gu.GEMV_REL, gu.GEMV_ABS)
+    assert r <= 1.0, f"tolerance ratio {r}"
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+def test_multi_invariants(oracle, fmt):
+    """Deterministic; doubling every scale doubles Y bit for bit; a one-hot
+    token row gives the weight column exactly as lq_dequant_f32 unpacks it;
+    each token row agrees with the single-token GEMV of that row."""
+    M, N, K = 16, 200, 2048 if fmt != "q4_0" else 896
+    say("gemv_multi invariants", fmt, M, N, K)
+    w, s = make(fmt, 4321, N, K)
+    X = lqgen.activations(77, M * K, np.float16).reshape(M, K)
+    Wd = gu.upload(fmt, w, s, N, K)
+    Y1 = gu.gemv_multi(fmt, Wd, X, M, N, K)
+    Y2 = gu.gemv_multi(fmt, Wd, X, M, N, K)
+    assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32)), "not deterministic"
+    if fmt == "i8b64":
+        w2, s2 = w, s * np.float32(2)
+    else:
+        bb = 18 if fmt == "q4_0" else 34
+        blk = w.reshape(-1, bb).copy()
+        d = blk[:, 0:2].copy().view(np.float16) * np.float16(2)
+        blk[:, 0:2] = d.view(np.uint8).reshape(-1, 2)
+        w2, s2 = blk.reshape(-1), None
+    Y3 = gu.gemv_multi(fmt, gu.upload(fmt, w2, s2, N, K), X, M, N, K)
+    assert np.array_equal(Y3, 2 * Y1)
+    out32 = torch.empty(N * K, dtype=torch.float32, device="cuda")
+    lq.lq_dequant_f32(gu.FMT[fmt], Wd, out32, N, K)
+    torch.cuda.synchronize()
+    full = out32.cpu().numpy().reshape(N, K)
+    ks = [0, 1, 15, 16, 31, 32, 63, 100, 257, 511, 640, K - 33, K - 17, K - 2, K - 1, 5]
+    E = np.zeros((M, K), np.float16)
+    for m, k in enumerate(ks):
+        E[m, k] = 1
+    Ye = gu.gemv_multi(fmt, Wd, E, M, N, K)
+    for m, k in enumerate(ks):
+        assert np.array_equal(Ye[m].view(np.uint32), full[:, k].view(np.uint32)), (m, k)
+    for m in (0, 7, 15):
+        y = gu.gemv(fmt, Wd, X[m], N, K)
+        _, S = oracle.gemv(ORACLE_FMT[fmt], w, s, X[m], N, K)
+        assert np.all(np.abs(Y1[m].astype(np.float64) - y) <= 2 * (gu.GEMV_REL * S + gu.GEMV_ABS)), m
+
+
+def test_multi_zero_codes():
+    """Q4_0 codes all 8 and Q8_0 / int8 codes all 0 give exactly zero."""
+    M, N, K = 9, 100, 2048
+    for fmt in ("q4_0", "q8_0", "i8b64"):
+        say("gemv_multi zero codes", fmt)
+        w, s = make(fmt, 5, N, K)
+        if fmt == "i8b64":
+            w = np.zeros_like(w)
+        else:
+            bb = 18 if fmt == "q4_0" else 34
+            blk = w.reshape(-1, bb).copy()
+            blk[:, 2:] = 0x88 if fmt == "q4_0" else 0
+            w = blk.reshape(-1)
+        X = lqgen.activations(3, M * K, np.float16).reshape(M, K)
+        Y = gu.gemv_multi(fmt, gu.upload(fmt, w, s, N, K), X, M, N, K)
+        assert np.all(Y == 0)
+
+
+def test_matmul_routes_few_tokens_to_multi():
+    """lq_matmul with 2..16 fp16 tokens is the multi-token GEMV, bit for bit."""
+    N, K = 96, 512
+    w, _ = make("q4_0", 12, N, K)
+    Wd = gu.upload("q4_0", w, None, N, K)
+    for M in (2, 9, 16):
+        say("matmul routing", M)
+        X = lqgen.activations(13 + M, M * K, np.float16).reshape(M, K)
+        Ym = gu.gemv_multi("q4_0", Wd, X, M, N, K)
+        Y = gu.guarded(M * N)
+        lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(X), Y, M, N, K)
+        torch.cuda.synchronize()
+        gu.check_guard(Y, M * N)
+        assert np.array_equal(Y[:M * N].cpu().numpy().reshape(M, N), Ym), M
+
+
+def test_multi_graph_replays_match_eager(oracle):
+    """Split-K multi-token launches captured in a graph: every replay equals
+    the eager result bit for bit, with eager runs in between."""
+    say("gemv_multi graph replays")
+    cases = [("q8_0", 16, 128, 4096), ("q4_0", 5, 64, 2048), ("i8b64", 3, 200, 5632)]
+    data, outs = [], []
+    for i, (fmt, M, N, K) in enumerate(cases):
+        w, s = make(fmt, 7100 + i, N, K)
+        X = lqgen.activations(7200 + i, M * K, np.float16).reshape(M, K)
+        data.append((fmt, M, N, K, w, s, X, gu.upload(fmt, w, s, N, K), to_device(X)))
+        outs.append(torch.zeros(M * N, device="cuda"))
+
+    def run():
+        for (fmt, M, N, K, _, _, _, Wd, Xd), Y in zip(data, outs):
+            lq.lq_gemv_multi(gu.FMT[fmt], Wd, Xd, Y, M, N, K)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for (fmt, M, N, K, w, s, X, _, _), Y in zip(data, eager):
+        Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K)
+        assert gu.ratio(Y.cpu().numpy().reshape(M, N), Yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, fmt
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs from the eager result"
+        run()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"eager run after replay {rep} differs"
+
+
+def _workload(oracle, wl, sample):
+    M = wl.M
+    worst = 0.0
+    for m in wl.mats:
+        say("gemv_multi workload", wl.name, m.name, M, m.N, m.K)
+        w, s = m.generate()
+        X = wl.x(m.xkey)
+        Wd = gu.upload(m.fmt, w, s, m.N, m.K)
+        Y = gu.gemv_multi(m.fmt, Wd, X, M, m.N, m.K)
+        rng = np.random.default_rng(m.seed)
+        ns = np.unique(np.concatenate([[0, 1, 63, 64, m.N - 2, m.N - 1], rng.integers(0, m.N, sample)]))
+        Yr, S = oracle.gemm(ORACLE_FMT[m.fmt], w, s, X, M, m.N, m.K, ns=ns)
+        r = gu.ratio(Y[:, ns], Yr, S, gu.GEMV_REL, gu.GEMV_ABS)
+        assert r <= 1.0, (wl.name, m.name, r)
+        worst = max(worst, r)
+        del Wd
+    return worst
+
+
+@pytest.mark.slow
+def test_workload_multi_lm_head(oracle):
+    _workload(oracle, lqgen.multi_token(lqgen.q4_0_lmhead_151936x896(), 16), 2048)
+
+
+@pytest.mark.slow
+def test_workload_multi_q8_0_layer(oracle):
+    _workload(oracle, lqgen.multi_token(lqgen.q8_0_layer_2048(0), 8), 1024)
+
+
+@pytest.mark.slow
+def test_workload_multi_i8b64_layer(oracle):
+    _workload(oracle, lqgen.multi_token(lqgen.i8b64_tinyllama_layer(0), 4), 1024)
