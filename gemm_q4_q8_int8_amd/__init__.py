@@ -22,7 +22,8 @@ FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64}
 # Every symbol include/lq.h declares.
 EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq_scale_offset",
            "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_dequant_f32",
-           "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi", "lq_gemm_workspace_bytes",
+           "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi", "lq_gemv_multi_batch",
+           "lq_gemm_workspace_bytes",
            "lq_gemm",
            "lq_matmul", "lq_status_str", "lq_last_error")
 
@@ -43,6 +44,12 @@ class lq_gemv_desc(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("xdt", ctypes.c_int32), ("W", ctypes.c_void_p),
                 ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64),
                 ("K", ctypes.c_int64)]
+
+
+class lq_gemv_multi_desc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("xdt", ctypes.c_int32), ("W", ctypes.c_void_p),
+                ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 _lib = None
@@ -71,6 +78,7 @@ def load(path: str = LIB_PATH):
         "lq_gemv": ([i32, vp, vp, i32, vp, i64, i64, vp], i32),
         "lq_gemv_batch": ([ctypes.POINTER(lq_gemv_desc), i32, vp], i32),
         "lq_gemv_multi": ([i32, vp, vp, i32, vp, i64, i64, i64, vp], i32),
+        "lq_gemv_multi_batch": ([ctypes.POINTER(lq_gemv_multi_desc), i32, vp], i32),
         "lq_gemm_workspace_bytes": ([i32, i64, i64, i64], sz),
         "lq_gemm": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_matmul": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
@@ -196,6 +204,14 @@ def lq_gemv_multi(fmt, W, X, Y, M, N, K, stream=None, xdt=None):
     xdt = _xdt(X) if xdt is None else xdt
     _check(load().lq_gemv_multi(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K,
                                 _stream(stream)))
+
+
+def lq_gemv_multi_batch(descs, stream=None):
+    """descs: sequence of (fmt, W, X, Y, M, N, K) tuples of tensors / sizes."""
+    arr = (lq_gemv_multi_desc * max(1, len(descs)))()
+    for i, (fmt, W, X, Y, M, N, K) in enumerate(descs):
+        arr[i] = lq_gemv_multi_desc(_fmt(fmt), _xdt(X), _ptr(W), _ptr(X), _ptr(Y), M, N, K)
+    _check(load().lq_gemv_multi_batch(arr, len(descs), _stream(stream)))
 
 
 def lq_gemm(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=0, stream=None, xdt=None):

@@ -27,9 +27,15 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  The multi-token GEMV takes its MFMA results in
+# ordinary VGPRs (the compiler otherwise routes them through accumulation
+# registers and copies each one back).
+EXTRA = {"lq_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass reports the packed-fp32 target feature as unknown; that
     # line is expected and harmless.

@@ -166,6 +166,92 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
     return LQ_OK;
 }
 
+lq_status check_multi_desc(const lq_gemv_multi_desc& d, int idx) {
+    lq_status st = check_fmt_shape(d.fmt, d.N, d.K);
+    if (st != LQ_OK) return st;
+    st = check_xdt(d.xdt);
+    if (st != LQ_OK) return st;
+    if (d.xdt != LQ_F16)
+        return fail(LQ_ERR_UNSUPPORTED, "descriptor %d: multi-token GEMV takes LQ_F16 activations", idx);
+    if (d.M < 1 || d.M > lq::kMultiMaxTokens)
+        return fail(LQ_ERR_SHAPE, "descriptor %d: M=%lld out of range [1, %d]", idx, (long long)d.M,
+                    lq::kMultiMaxTokens);
+    if (!d.W || !d.X || !d.Y) return fail(LQ_ERR_ARG, "descriptor %d: W, X or Y is NULL", idx);
+    if (!aligned(d.W, 16) || !aligned(d.X, 16))
+        return fail(LQ_ERR_ALIGN, "descriptor %d: W and X must be 16-byte aligned", idx);
+    if (!aligned(d.Y, 4)) return fail(LQ_ERR_ALIGN, "descriptor %d: Y must be 4-byte aligned", idx);
+    return LQ_OK;
+}
+
+// One grouped multi-token launch: up to kMaxBatch descriptors of one format.
+// The K split follows the single-token rule, with the partials of M tokens
+// per row counted against the scratch area.
+lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc*>& g, int cus,
+                             hipStream_t stream) {
+    const int n = int(g.size());
+    std::vector<int64_t> tiles(n), nu(n), S(n, 1);
+    int64_t total_tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        tiles[i] = (g[i]->N + lq::kTileRows - 1) / lq::kTileRows;
+        nu[i] = g[i]->K / lq::unit_elems(fmt);
+        total_tiles += tiles[i];
+    }
+    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
+    if (total_tiles < target) {
+        const int64_t want = (target + total_tiles - 1) / total_tiles;
+        int64_t part = 0, cnt = 0;
+        for (int i = 0; i < n; ++i) {
+            S[i] = std::min(want, std::max<int64_t>(1, nu[i] / (4 * LQ_GEMV_MIN_UNITS)));
+            if (S[i] > 1) {
+                part += S[i] * g[i]->M * tiles[i] * lq::kTileRows;
+                cnt += tiles[i];
+            }
+        }
+        if (part > lq::kGemvPartFloats || cnt > lq::kGemvCounters)
+            for (int i = 0; i < n; ++i) S[i] = 1;
+    }
+    float* part = nullptr;
+    uint32_t* cntp = nullptr;
+    bool any_split = false;
+    for (int i = 0; i < n; ++i) any_split = any_split || S[i] > 1;
+    if (any_split) {
+        const hipError_t e = lq::gemv_scratch(&part, &cntp);
+        if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
+    }
+    lq::MultiArgs a = {};
+    int64_t wgs = 0, part_off = 0, cnt_off = 0;
+    for (int i = 0; i < n; ++i) {
+        const lq_gemv_multi_desc& d = *g[i];
+        lq::MultiDesc& o = a.d[i];
+        o.codes = static_cast<const uint8_t*>(d.W);
+        o.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(fmt, d.N, d.K));
+        o.x = static_cast<const _Float16*>(d.X);
+        o.y = d.Y;
+        o.N = int32_t(d.N);
+        o.K = int32_t(d.K);
+        o.nu = int32_t(nu[i]);
+        o.tiles = int32_t(tiles[i]);
+        o.S = int32_t(S[i]);
+        o.M = int32_t(d.M);
+        o.vec_y = (aligned(d.Y, 16) && d.N % 4 == 0) ? 1 : 0;
+        o.wg0 = int32_t(wgs);
+        o.part = nullptr;
+        o.cnt = nullptr;
+        if (S[i] > 1) {
+            o.part = part + part_off;
+            o.cnt = cntp + cnt_off;
+            part_off += S[i] * d.M * tiles[i] * lq::kTileRows;
+            cnt_off += tiles[i];
+        }
+        wgs += tiles[i] * S[i];
+        if (wgs > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
+    }
+    a.count = n;
+    a.total_wgs = int32_t(wgs);
+    const hipError_t e = lq::launch_gemv_multi(fmt, a, stream);
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "multi-token GEMV launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,47 +360,44 @@ lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt, float*
     return lq_gemv_batch(&d, 1, stream);
 }
 
-lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
-                        int64_t N, int64_t K, void* stream) {
-    LQ_TRY(check_fmt_shape(fmt, N, K));
-    LQ_TRY(check_xdt(xdt));
-    if (xdt != LQ_F16) return fail(LQ_ERR_UNSUPPORTED, "lq_gemv_multi takes LQ_F16 activations");
-    if (M < 1 || M > lq::kMultiMaxTokens)
-        return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, %d]", (long long)M, lq::kMultiMaxTokens);
-    LQ_TRY(check_ptr(W, 16, "W"));
-    LQ_TRY(check_ptr(X, 16, "X"));
-    LQ_TRY(check_ptr(Y, 4, "Y"));
+lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* stream) {
+    if (!descs) return fail(LQ_ERR_ARG, "descs is NULL");
+    if (count < 1) return fail(LQ_ERR_ARG, "count=%d must be >= 1", count);
+    for (int32_t i = 0; i < count; ++i) LQ_TRY(check_multi_desc(descs[i], i));
     int cus = 0;
     LQ_TRY(device_cus(&cus));
-    const int64_t tiles = (N + lq::kTileRows - 1) / lq::kTileRows;
-    const int64_t nu = K / lq::unit_elems(fmt);
-    // K split as for the single-token GEMV, bounded by the scratch area.
-    int64_t S = 1;
-    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
-    if (tiles < target) {
-        S = std::min((target + tiles - 1) / tiles, std::max<int64_t>(1, nu / (4 * LQ_GEMV_MIN_UNITS)));
-        S = std::min(S, std::max<int64_t>(1, lq::kGemvPartFloats / (M * tiles * lq::kTileRows)));
-        if (tiles > lq::kGemvCounters) S = 1;
+    // Group by format, keeping order, in chunks of kMaxBatch.
+    std::vector<bool> done(size_t(count), false);
+    for (int32_t i = 0; i < count; ++i) {
+        if (done[i]) continue;
+        std::vector<const lq_gemv_multi_desc*> chunk;
+        for (int32_t j = i; j < count; ++j) {
+            if (done[j] || descs[j].fmt != descs[i].fmt) continue;
+            chunk.push_back(&descs[j]);
+            done[j] = true;
+            if (chunk.size() == size_t(lq::kMaxBatch)) {
+                LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, static_cast<hipStream_t>(stream)));
+                chunk.clear();
+            }
+        }
+        if (!chunk.empty())
+            LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, static_cast<hipStream_t>(stream)));
     }
-    if (tiles * S > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows");
-    lq::MultiDesc d = {};
-    d.codes = static_cast<const uint8_t*>(W);
-    d.scales = static_cast<const uint8_t*>(W) + lq::align256(lq::code_plane_bytes(fmt, N, K));
-    d.x = static_cast<const _Float16*>(X);
-    d.y = Y;
-    d.N = int32_t(N);
-    d.K = int32_t(K);
-    d.nu = int32_t(nu);
-    d.tiles = int32_t(tiles);
-    d.S = int32_t(S);
-    d.M = int32_t(M);
-    d.vec_y = (aligned(Y, 16) && N % 4 == 0) ? 1 : 0;
-    if (S > 1) {
-        const hipError_t e = lq::gemv_scratch(&d.part, &d.cnt);
-        if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
-    }
-    const hipError_t e = lq::launch_gemv_multi(fmt, d, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? LQ_OK : hip_fail(e, "multi-token GEMV launch");
+    return LQ_OK;
+}
+
+lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
+                        int64_t N, int64_t K, void* stream) {
+    lq_gemv_multi_desc d;
+    d.fmt = fmt;
+    d.xdt = xdt;
+    d.W = W;
+    d.X = X;
+    d.Y = Y;
+    d.M = M;
+    d.N = N;
+    d.K = K;
+    return lq_gemv_multi_batch(&d, 1, stream);
 }
 
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {

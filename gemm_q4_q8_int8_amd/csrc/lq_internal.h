@@ -111,10 +111,10 @@ hipError_t gemv_scratch(float** part, uint32_t** cnt);
 constexpr int kMultiMaxTokens = 16;   // tokens of one MFMA fragment
 // Units whose loads one wave issues before computing them (per format).
 #ifndef LQ_MULTI_UNR_Q4
-#define LQ_MULTI_UNR_Q4 8
+#define LQ_MULTI_UNR_Q4 4
 #endif
 #ifndef LQ_MULTI_UNR_Q8
-#define LQ_MULTI_UNR_Q8 4
+#define LQ_MULTI_UNR_Q8 2
 #endif
 #ifndef LQ_MULTI_UNR_I8
 #define LQ_MULTI_UNR_I8 2
@@ -134,10 +134,16 @@ struct MultiDesc {
     int32_t S;              // K slices (workgroups per tile)
     int32_t M;              // tokens, 1 .. kMultiMaxTokens
     int32_t vec_y;          // y rows are 16-byte aligned: full tiles store float4
-    int32_t pad;
+    int32_t wg0;            // first workgroup of this matrix in the launch
 };
 
-hipError_t launch_gemv_multi(int fmt, const MultiDesc& d, hipStream_t stream);
+struct MultiArgs {
+    MultiDesc d[kMaxBatch];
+    int32_t count;
+    int32_t total_wgs;
+};
+
+hipError_t launch_gemv_multi(int fmt, const MultiArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------- conversions ----
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,

@@ -124,8 +124,107 @@ struct MUnit {
     static constexpr int KS = steps_of<FMT>();
     u32x4 c[P];          // codes of tile row 4r + g (this lane's load)
     u32x2 xl[KS], xh[KS];  // activations of this lane's token and k-set
-    uint32_t s[4];       // raw scales of rows 4r .. 4r+3
+    // Raw scales of rows 4r .. 4r+3, as loaded: fp32 in s[0..3]; fp16 as two
+    // packed dwords s[0..1] (full tile) or one per dword (partial tile).
+    // Unpacking waits until use so that no ALU op follows a load directly
+    // (it would make the load phase wait for its data).
+    uint32_t s[4];
 };
+
+// fp32 scale of row 4r + m.
+template <int FMT, bool FULL>
+__device__ __forceinline__ float scale_of(const MUnit<FMT>& b, int m) {
+    if constexpr (scale_bytes(FMT) == 4) {
+        return __uint_as_float(b.s[m]);
+    } else {
+        const uint32_t v = FULL ? b.s[m >> 1] : b.s[m];
+        const uint16_t h = uint16_t(FULL && (m & 1) ? v >> 16 : v);
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+}
+
+// Where one wave reads: tile bases, per-lane offsets and its unit range.
+struct WaveLoop {
+    const uint8_t* cbase;   // code plane of the tile
+    const uint8_t* sbase;   // scale plane of the tile
+    const _Float16* xrow;   // activations of this lane's token at its k-set
+    uint32_t c_lane, c_unit, c_part, s_unit;
+    uint32_t s_row[4];      // scale offsets of rows 4r .. 4r+3 (clamped)
+    int ua, ub;             // units [ua, ub)
+};
+
+// acc[m][i] += sum over the wave's units of w[4r+m, k] X[4j+i, k].  FULL: the
+// tile has 64 rows, so the four scales of rows 4r..4r+3 are one load.  The
+// choice is made once per workgroup so the load phase has no branches.
+template <int FMT, bool FULL>
+__device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
+    constexpr int P = unit_parts(FMT);
+    constexpr int SB = scale_bytes(FMT);
+    constexpr int E = unit_elems(FMT);
+    constexpr int KS = steps_of<FMT>();
+    constexpr int UNR = multi_unroll<FMT>();
+    for (int u = L.ua; u < L.ub; u += UNR) {
+        MUnit<FMT> b[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t uu = uint32_t(min(u + k, L.ub - 1));
+            const uint32_t co = uu * L.c_unit + L.c_lane;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                b[k].c[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
+            const uint8_t* sp = L.sbase + uu * L.s_unit;
+            if constexpr (FULL && SB == 2) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(sp + L.s_row[0]);
+                b[k].s[0] = v.x;
+                b[k].s[1] = v.y;
+            } else if constexpr (FULL) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(sp + L.s_row[0]);
+                b[k].s[0] = v.x;
+                b[k].s[1] = v.y;
+                b[k].s[2] = v.z;
+                b[k].s[3] = v.w;
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if constexpr (SB == 2) b[k].s[m] = *reinterpret_cast<const uint16_t*>(sp + L.s_row[m]);
+                    else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + L.s_row[m]);
+                }
+            }
+            const _Float16* xp = L.xrow + size_t(uu) * E;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                b[k].xl[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks);
+                b[k].xh[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks + 16);
+            }
+        }
+        // Every load of the batch is issued before any of its data is used.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            if (u + k >= L.ub) continue;
+            u32x4 t[P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) t[p] = xpose(b[k].c[p]);
+            half8_t xa[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) xa[ks] = x_frag<FMT>(b[k].xl[ks], b[k].xh[ks]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    half8_t wb;
+                    if constexpr (FMT == kQ4_0) wb = q4_frag(t[0][m]);
+                    else wb = i8_frag(t[2 * ks][m], t[2 * ks + 1][m]);
+                    sum = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ks], wb, sum, 0, 0, 0);
+                }
+                const float d = scale_of<FMT, FULL>(b[k], m);
+                acc[m] = __builtin_elementwise_fma(f32x4{d, d, d, d}, sum, acc[m]);
+            }
+        }
+    }
+}
 
 // sum_{j < S} p[j * pitch] in slice order (eight loads in flight).
 __device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S) {
@@ -144,19 +243,22 @@ __device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S)
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiDesc D) {
-    constexpr int P = unit_parts(FMT);
+__global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArgs a) {
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
-    constexpr int E = unit_elems(FMT);
-    constexpr int KS = steps_of<FMT>();
-    constexpr int UNR = multi_unroll<FMT>();
     __shared__ float red[4][16][64];
     __shared__ uint32_t arrival;
 
+    // Matrix of this workgroup: the last descriptor whose first workgroup is
+    // not after ours (uniform, scalar compares).
+    const int bid = int(blockIdx.x);
+    int di = 0;
+    for (int i = 1; i < a.count; ++i) di += bid >= a.d[i].wg0 ? 1 : 0;
+    const MultiDesc& D = a.d[di];
     const int N = D.N, nu = D.nu, S = D.S, M = D.M;
-    const int tile = int(blockIdx.x) / S;
-    const int slice = int(blockIdx.x) - tile * S;
+    const int local = bid - D.wg0;
+    const int tile = local / S;
+    const int slice = local - tile * S;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int lane = int(threadIdx.x) & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -169,85 +271,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiDes
     const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / 4);
 
     const size_t first = size_t(tile) * kTileRows * size_t(nu);
-    const uint8_t* cbase = D.codes + first * UB;
-    const uint8_t* sbase = D.scales + first * SB;
+    WaveLoop L;
+    L.cbase = D.codes + first * UB;
+    L.sbase = D.scales + first * SB;
     // Rows past the end of a partial tile are re-read from the last row and
     // never stored; so are tokens past M.
-    const uint32_t c_lane = uint32_t(min(4 * r + g, nr - 1)) * 16u;
-    const uint32_t c_unit = uint32_t(nr) * UB;
-    const uint32_t c_part = uint32_t(nr) * 16u;
-    const uint32_t s_unit = uint32_t(nr) * SB;
-    uint32_t s_row[4];
+    L.c_lane = uint32_t(min(4 * r + g, nr - 1)) * 16u;
+    L.c_unit = uint32_t(nr) * UB;
+    L.c_part = uint32_t(nr) * 16u;
+    L.s_unit = uint32_t(nr) * SB;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
-    const _Float16* xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + 4 * g;
+    for (int m = 0; m < 4; ++m) L.s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
+    L.xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + 4 * g;
+    L.ua = ua;
+    L.ub = ub;
 
     f32x4 acc[4] = {};
-    for (int u = ua; u < ub; u += UNR) {
-        MUnit<FMT> b[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const uint32_t uu = uint32_t(min(u + k, ub - 1));
-            const uint32_t co = uu * c_unit + c_lane;
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                b[k].c[p] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(cbase + co + uint32_t(p) * c_part));
-            const uint8_t* sp = sbase + uu * s_unit;
-            if (full) {
-                if constexpr (SB == 2) {
-                    const u32x2 v = *reinterpret_cast<const u32x2*>(sp + s_row[0]);
-                    b[k].s[0] = v.x & 0xFFFFu;
-                    b[k].s[1] = v.x >> 16;
-                    b[k].s[2] = v.y & 0xFFFFu;
-                    b[k].s[3] = v.y >> 16;
-                } else {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(sp + s_row[0]);
-                    b[k].s[0] = v.x;
-                    b[k].s[1] = v.y;
-                    b[k].s[2] = v.z;
-                    b[k].s[3] = v.w;
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if constexpr (SB == 2) b[k].s[m] = *reinterpret_cast<const uint16_t*>(sp + s_row[m]);
-                    else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + s_row[m]);
-                }
-            }
-            const _Float16* xp = xrow + size_t(uu) * E;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                b[k].xl[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks);
-                b[k].xh[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks + 16);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            if (u + k >= ub) continue;
-            u32x4 t[P];
-#pragma unroll
-            for (int p = 0; p < P; ++p) t[p] = xpose(b[k].c[p]);
-            half8_t xa[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) xa[ks] = x_frag<FMT>(b[k].xl[ks], b[k].xh[ks]);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    half8_t wb;
-                    if constexpr (FMT == kQ4_0) wb = q4_frag(t[0][m]);
-                    else wb = i8_frag(t[2 * ks][m], t[2 * ks + 1][m]);
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ks], wb, s, 0, 0, 0);
-                }
-                float d;
-                if constexpr (SB == 4) d = __uint_as_float(b[k].s[m]);
-                else d = (float)__builtin_bit_cast(_Float16, uint16_t(b[k].s[m]));
-                acc[m] = __builtin_elementwise_fma(f32x4{d, d, d, d}, s, acc[m]);
-            }
-        }
-    }
+    if (full) accumulate<FMT, true>(L, acc);
+    else accumulate<FMT, false>(L, acc);
 
     // Sum the four waves' K quarters; wave w then owns token 4g + w of rows
     // 4r .. 4r+3.
@@ -307,12 +348,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiDes
 
 }  // namespace
 
-hipError_t launch_gemv_multi(int fmt, const MultiDesc& d, hipStream_t stream) {
-    const dim3 grid(unsigned(d.tiles) * unsigned(d.S)), block(kGemvThreads);
+hipError_t launch_gemv_multi(int fmt, const MultiArgs& a, hipStream_t stream) {
+    const dim3 grid(unsigned(a.total_wgs)), block(kGemvThreads);
     switch (fmt) {
-        case kQ4_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ4_0>, grid, block, 0, stream, d); break;
-        case kQ8_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ8_0>, grid, block, 0, stream, d); break;
-        case kI8B64: hipLaunchKernelGGL(gemv_multi_kernel<kI8B64>, grid, block, 0, stream, d); break;
+        case kQ4_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ4_0>, grid, block, 0, stream, a); break;
+        case kQ8_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ8_0>, grid, block, 0, stream, a); break;
+        case kI8B64: hipLaunchKernelGGL(gemv_multi_kernel<kI8B64>, grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -189,6 +189,27 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
 lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt,
                         float* Y, int64_t M, int64_t N, int64_t K, void* stream);
 
+/* One independent multi-token GEMV for lq_gemv_multi_batch (fields as in
+ * lq_gemv_multi; M may differ between descriptors). */
+typedef struct lq_gemv_multi_desc {
+    int32_t fmt;
+    int32_t xdt;
+    const void* W;
+    const void* X;
+    float* Y;
+    int64_t M;
+    int64_t N;
+    int64_t K;
+} lq_gemv_multi_desc;
+
+/* Grouped launch of `count` independent multi-token GEMVs (for example every
+ * projection of a decoder layer verifying the same drafted tokens), so that
+ * small matrices share launches.  descs: HOST array of `count` descriptors
+ * (count >= 1), read during the call only; all are validated before anything
+ * is enqueued.  Descriptors of one format run in one kernel launch (up to 16
+ * per launch). */
+lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* stream);
+
 /* Workspace bytes lq_gemm needs for these arguments (0 means none). */
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 

@@ -104,6 +104,15 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_gemv_multi(0, A16, None, 1, A16, 4, 64, 32, None) == ARG
     assert g.lq_gemv_multi(0, A16, A16, 3, A16, 4, 64, 32, None) == DTYPE
     assert g.lq_matmul(0, A16, A16, 1, A16, 4, 64, 48, None, 0, None) == SHAPE
+    md = (lq.lq_gemv_multi_desc * 2)()
+    md[0] = lq.lq_gemv_multi_desc(0, 1, A16, A16, A16, 4, 64, 32)
+    md[1] = lq.lq_gemv_multi_desc(1, 1, A16, A16, A16, 17, 64, 32)
+    assert g.lq_gemv_multi_batch(md, 0, None) == ARG
+    assert g.lq_gemv_multi_batch(None, 1, None) == ARG
+    assert g.lq_gemv_multi_batch(md, 2, None) == SHAPE          # second descriptor: M = 17
+    md[1] = lq.lq_gemv_multi_desc(1, 0, A16, A16, A16, 4, 64, 32)
+    assert g.lq_gemv_multi_batch(md, 2, None) == UNSUP          # fp32 activations
+    assert "descriptor 1" in lq.lq_last_error()
     # conversions
     assert g.lq_repack_gguf(2, A16, A16, 4, 64, None) == FMT
     assert g.lq_repack_gguf(0, A16 + 1, A16, 4, 64, None) == ALIGN

@@ -119,6 +119,37 @@ def test_multi_zero_codes():
         assert np.all(Y == 0)
 
 
+def test_multi_batch_mixed(oracle):
+    """Three formats, token counts 1..16, split and unsplit matrices, more
+    descriptors than one launch holds: every output, grouped and alone,
+    passes the oracle (the K split may differ between the two)."""
+    cases = []
+    for i in range(19):
+        fmt = ["q4_0", "q8_0", "i8b64"][i % 3]
+        K = [64, 896, 2048, 5632][i % 4] if fmt != "i8b64" else [64, 2048, 5632][i % 3]
+        N = 11 + 53 * i
+        M = 1 + (5 * i) % 16
+        w, s = make(fmt, 800 + i, N, K)
+        X = lqgen.activations(1900 + i, M * K, np.float16).reshape(M, K)
+        cases.append((fmt, M, N, K, w, s, X))
+    say("gemv_multi batch of", len(cases))
+    descs, outs, devs = [], [], []
+    for fmt, M, N, K, w, s, X in cases:
+        Wd, Xd, Y = gu.upload(fmt, w, s, N, K), to_device(X), gu.guarded(M * N)
+        devs.append((Wd, Xd))
+        descs.append((gu.FMT[fmt], Wd, Xd, Y, M, N, K))
+        outs.append(Y)
+    lq.lq_gemv_multi_batch(descs)
+    torch.cuda.synchronize()
+    for (fmt, M, N, K, w, s, X), Y, (Wd, Xd) in zip(cases, outs, devs):
+        gu.check_guard(Y, M * N)
+        got = Y[:M * N].cpu().numpy().reshape(M, N)
+        Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K)
+        assert gu.ratio(got, Yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, (fmt, M, N, K)
+        single = gu.gemv_multi(fmt, Wd, X, M, N, K)
+        assert gu.ratio(single, Yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, (fmt, M, N, K)
+
+
 def test_matmul_routes_few_tokens_to_multi():
     """lq_matmul with 2..16 fp16 tokens is the multi-token GEMV, bit for bit."""
     N, K = 96, 512
