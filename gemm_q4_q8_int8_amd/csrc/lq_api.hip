@@ -93,38 +93,51 @@ lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
     return LQ_OK;
 }
 
+// K split of a grouped GEMV launch (single- or multi-token): S[i] workgroups
+// share each 64-row tile of matrix i.  When the launch has fewer tiles than
+// about LQ_GEMV_WGS_PER_CU workgroups per CU, every matrix is split so that
+// its workgroups get about the same number of units (the launch's total work
+// spread over that many workgroups), never below LQ_GEMV_MIN_UNITS units per
+// wave.  Equal work per workgroup keeps a long-K matrix from becoming the
+// tail of the launch.  M[i] tokens of partials per row count against the
+// split-K scratch; if it does not fit, nothing is split.
+void split_k(int cus, const std::vector<int64_t>& tiles, const std::vector<int64_t>& nu,
+             const std::vector<int64_t>& M, std::vector<int64_t>& S) {
+    const size_t n = tiles.size();
+    int64_t total_tiles = 0, work = 0;
+    for (size_t i = 0; i < n; ++i) {
+        total_tiles += tiles[i];
+        work += tiles[i] * nu[i];
+        S[i] = 1;
+    }
+    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
+    if (total_tiles >= target) return;
+    const double per_wg = double(work) / double(target);   // units per workgroup
+    int64_t part = 0, cnt = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const int64_t cap = std::max<int64_t>(1, nu[i] / (4 * LQ_GEMV_MIN_UNITS));
+        const int64_t want = std::max<int64_t>(1, int64_t(double(nu[i]) / per_wg + 0.5));
+        S[i] = std::min(want, cap);
+        if (S[i] > 1) {
+            part += S[i] * M[i] * tiles[i] * lq::kTileRows;
+            cnt += tiles[i];
+        }
+    }
+    if (part > lq::kGemvPartFloats || cnt > lq::kGemvCounters)
+        for (size_t i = 0; i < n; ++i) S[i] = 1;
+}
+
 // One grouped GEMV launch: up to kMaxBatch descriptors of one format and
-// activation dtype.  Chooses the K split S (workgroups per 64-row tile) so
-// the launch has about LQ_GEMV_WGS_PER_CU workgroups per CU, keeping at least
-// LQ_GEMV_MIN_UNITS units per wave and the partials within the scratch area.
+// activation dtype, K split by split_k.
 lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>& g, int cus,
                        hipStream_t stream) {
     const int n = int(g.size());
     std::vector<int64_t> tiles(n), nu(n), S(n, 1);
-    int64_t total_tiles = 0;
     for (int i = 0; i < n; ++i) {
         tiles[i] = (g[i]->N + lq::kTileRows - 1) / lq::kTileRows;
         nu[i] = g[i]->K / lq::unit_elems(fmt);
-        total_tiles += tiles[i];
     }
-    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
-    if (total_tiles < target) {
-        const int64_t want = (target + total_tiles - 1) / total_tiles;
-        int64_t part = 0, cnt = 0;
-        for (int i = 0; i < n; ++i) {
-            const int64_t cap = std::max<int64_t>(1, nu[i] / (4 * LQ_GEMV_MIN_UNITS));
-            S[i] = std::min(want, cap);
-            if (S[i] > 1) {
-                part += S[i] * tiles[i] * lq::kTileRows;
-                cnt += tiles[i];
-            }
-        }
-        if (part > lq::kGemvPartFloats || cnt > lq::kGemvCounters) {
-            // Too large to split within the scratch area: no split at all
-            // (such matrices have enough tiles to fill the chip anyway).
-            for (int i = 0; i < n; ++i) S[i] = 1;
-        }
-    }
+    split_k(cus, tiles, nu, std::vector<int64_t>(n, 1), S);
     float* part = nullptr;
     uint32_t* cntp = nullptr;
     bool any_split = false;
@@ -190,26 +203,13 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
                              hipStream_t stream) {
     const int n = int(g.size());
     std::vector<int64_t> tiles(n), nu(n), S(n, 1);
-    int64_t total_tiles = 0;
     for (int i = 0; i < n; ++i) {
         tiles[i] = (g[i]->N + lq::kTileRows - 1) / lq::kTileRows;
         nu[i] = g[i]->K / lq::unit_elems(fmt);
-        total_tiles += tiles[i];
     }
-    const int64_t target = int64_t(cus) * LQ_GEMV_WGS_PER_CU;
-    if (total_tiles < target) {
-        const int64_t want = (target + total_tiles - 1) / total_tiles;
-        int64_t part = 0, cnt = 0;
-        for (int i = 0; i < n; ++i) {
-            S[i] = std::min(want, std::max<int64_t>(1, nu[i] / (4 * LQ_GEMV_MIN_UNITS)));
-            if (S[i] > 1) {
-                part += S[i] * g[i]->M * tiles[i] * lq::kTileRows;
-                cnt += tiles[i];
-            }
-        }
-        if (part > lq::kGemvPartFloats || cnt > lq::kGemvCounters)
-            for (int i = 0; i < n; ++i) S[i] = 1;
-    }
+    std::vector<int64_t> Ms(n);
+    for (int i = 0; i < n; ++i) Ms[i] = g[i]->M;
+    split_k(cus, tiles, nu, Ms, S);
     float* part = nullptr;
     uint32_t* cntp = nullptr;
     bool any_split = false;
