@@ -79,7 +79,7 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #define LQ_GEMV_UNR_I8 2
 #endif
 #ifndef LQ_GEMV_MIN_UNITS
-#define LQ_GEMV_MIN_UNITS 4
+#define LQ_GEMV_MIN_UNITS 2
 #endif
 
 struct GemvDesc {
