@@ -400,9 +400,17 @@ lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, 
     return lq_gemv_multi_batch(&d, 1, stream);
 }
 
+namespace {
+bool use_lds_tile_gemm(int32_t fmt) { return fmt == LQ_Q4_0 && !LQ_GEMM_Q4_PREFILL; }
+
+size_t gemm_ws(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+    return use_lds_tile_gemm(fmt) ? lq::gemm_workspace_bytes(M, N, K) : lq::prefill_workspace_bytes(M, N, K);
+}
+}  // namespace
+
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
-    if (check_fmt_shape(fmt, N, K) != LQ_OK || M < 1) return 0;
-    return lq::gemm_workspace_bytes(M, N, K);
+    if (check_fmt_shape(fmt, N, K) != LQ_OK || M < 1 || M > kMaxDim) return 0;
+    return gemm_ws(fmt, M, N, K);
 }
 
 lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
@@ -410,19 +418,20 @@ lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt, float*
     LQ_TRY(check_fmt_shape(fmt, N, K));
     LQ_TRY(check_xdt(xdt));
     if (M < 1 || M > kMaxDim) return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, 2^31-1]", (long long)M);
-    if (fmt != LQ_Q4_0 || xdt != LQ_F16)
-        return fail(LQ_ERR_UNSUPPORTED, "lq_gemm implements LQ_Q4_0 weights with LQ_F16 activations");
+    if (xdt != LQ_F16) return fail(LQ_ERR_UNSUPPORTED, "lq_gemm takes LQ_F16 activations");
+    if (M * K > (int64_t(1) << 40)) return fail(LQ_ERR_SHAPE, "X too large");
     LQ_TRY(check_ptr(W, 16, "W"));
     LQ_TRY(check_ptr(X, 16, "X"));
     LQ_TRY(check_ptr(Y, 4, "Y"));
-    const size_t need = lq::gemm_workspace_bytes(M, N, K);
+    const size_t need = gemm_ws(fmt, M, N, K);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, ws_bytes);
     if (ws && !aligned(ws, 16)) return fail(LQ_ERR_ALIGN, "ws is not 16-byte aligned");
     int cus = 0;
     LQ_TRY(device_cus(&cus));
-    const hipError_t e = lq::launch_gemm_q4_0(W, X, Y, M, N, K, ws, ws_bytes, cus,
-                                              static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = use_lds_tile_gemm(fmt) ? lq::launch_gemm_q4_0(W, X, Y, M, N, K, ws, ws_bytes, cus, s)
+                                                : lq::launch_prefill(fmt, W, X, Y, M, N, K, ws, s);
     return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
 }
 

@@ -343,6 +343,12 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     return p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
 }
 
+hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipStream_t stream) {
+    const size_t blocks = (mn + 1023) / 1024;
+    hipLaunchKernelGGL(splitk_reduce, dim3(unsigned(blocks)), dim3(256), 0, stream, P, Y, mn, S);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_q4_0(const void* W, const void* X, float* Y, int64_t M, int64_t N,
                             int64_t K, void* ws, size_t, int, hipStream_t stream) {
     const Plan p = plan_gemm(M, N, K);
@@ -379,11 +385,7 @@ hipError_t launch_gemm_q4_0(const void* W, const void* X, float* Y, int64_t M, i
     hipLaunchKernelGGL(gemm_q4_0_kernel, dim3(unsigned(grid)), dim3(kThreads), kLdsBytes, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.S == 1) return e;
-    const size_t mn = size_t(M) * size_t(N);
-    const size_t blocks = (mn + 1023) / 1024;
-    hipLaunchKernelGGL(splitk_reduce, dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const float*>(ws), Y, mn, p.S);
-    return hipGetLastError();
+    return launch_splitk_reduce(static_cast<const float*>(ws), Y, size_t(M) * size_t(N), p.S, stream);
 }
 
 }  // namespace lq

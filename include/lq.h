@@ -213,13 +213,18 @@ lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, vo
 /* Workspace bytes lq_gemm needs for these arguments (0 means none). */
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 
-/* Prefill GEMM: Y[m,n] = sum_k RN_fp16(w[n,k]) * X[m,k], products and sums in
- * fp32 on the matrix cores.  W: packed N x K; X: M x K fp16 row-major;
- * Y: M x N fp32 row-major.  ws / ws_bytes: workspace of at least
- * lq_gemm_workspace_bytes() bytes (may be NULL when that is 0).  Accuracy:
- * |Y - Y_exact| <= 2e-3 * sum_k |w x| + 1e-5 per element.  This version
- * implements fmt LQ_Q4_0 with xdt LQ_F16; other combinations return
- * LQ_ERR_UNSUPPORTED. */
+/* Prefill GEMM ("oxinfer" page, "Performance": prefill is compute bound;
+ * "Platforms and accelerators": weights dequantized on chip for a dense tile
+ * product), all three formats, fp16 X (xdt must be LQ_F16, else
+ * LQ_ERR_UNSUPPORTED), products and sums in fp32 on the matrix cores:
+ *   LQ_Q4_0, LQ_Q8_0:  Y[m,n] = sum_k RN_fp16(w[n,k]) * X[m,k]
+ *                      (the fp16 tile of lq_dequant_f16);
+ *   LQ_I8B64:          Y[m,n] = sum_blocks s * sum_k c[n,k] * X[m,k]
+ *                      (codes exact, fp32 scale applied to block sums).
+ * W: packed N x K; X: M x K fp16 row-major; Y: M x N fp32 row-major.
+ * ws / ws_bytes: workspace of at least lq_gemm_workspace_bytes() bytes (may
+ * be NULL when that is 0).  Accuracy: |Y - Y_exact| <= 2e-3 * sum_k |w x| +
+ * 1e-5 per element. */
 lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt,
                   float* Y, int64_t M, int64_t N, int64_t K,
                   void* ws, size_t ws_bytes, void* stream);

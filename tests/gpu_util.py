@@ -66,12 +66,12 @@ def gemv(fmt: str, Wd, x: np.ndarray, N, K):
     return y[:N].cpu().numpy()
 
 
-def gemm(Wd, X: np.ndarray, M, N, K):
+def gemm(Wd, X: np.ndarray, M, N, K, fmt: str = "q4_0"):
     Xd = to_device(X)
     Y = guarded(M * N)
-    ws_bytes = lq.lq_gemm_workspace_bytes(lq.LQ_Q4_0, M, N, K)
+    ws_bytes = lq.lq_gemm_workspace_bytes(FMT[fmt], M, N, K)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
-    lq.lq_gemm(lq.LQ_Q4_0, Wd, Xd, Y, M, N, K, ws=ws, ws_bytes=ws_bytes)
+    lq.lq_gemm(FMT[fmt], Wd, Xd, Y, M, N, K, ws=ws, ws_bytes=ws_bytes)
     torch.cuda.synchronize()
     check_guard(Y, M * N)
     return Y[:M * N].cpu().numpy().reshape(M, N)

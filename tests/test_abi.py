@@ -87,8 +87,9 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_gemv_batch(None, 1, None) == ARG
     assert g.lq_gemv_batch(d, 2, None) == SHAPE
     # gemm
-    assert g.lq_gemm(1, A16, A16, 1, A16, 16, 32, 32, None, 0, None) == UNSUP
-    assert g.lq_gemm(0, A16, A16, 0, A16, 16, 32, 32, None, 0, None) == UNSUP
+    assert g.lq_gemm(0, A16, A16, 0, A16, 16, 32, 32, None, 0, None) == UNSUP     # fp32 X
+    assert g.lq_gemm(2, A16, A16, 1, A16, 16, 32, 32, None, 0, None) == SHAPE     # int8 block 64
+    assert g.lq_gemm(1, A16, A16, 1, A16 + 2, 16, 32, 32, None, 0, None) == ALIGN
     assert g.lq_gemm(0, A16, A16, 1, A16, 0, 32, 32, None, 0, None) == SHAPE
     assert g.lq_gemm(0, A16, A16 + 2, 1, A16, 16, 32, 32, None, 0, None) == ALIGN
     assert g.lq_gemm(0, A16, A16, 7, A16, 16, 32, 32, None, 0, None) == DTYPE

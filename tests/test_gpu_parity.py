@@ -377,6 +377,58 @@ def test_gemm_parity(oracle, M, N, K):
     assert gu.ratio(Y, Yt, St, 1e-4, 1e-6) <= 1.0
 
 
+# Q8_0 and int8 block-64 prefill: row, column and K tails, K split across
+# workgroups, several token blocks.
+GEMM_INT8_SHAPES = [(16, 64, 64), (5, 33, 128), (130, 129, 256), (1, 128, 64), (200, 300, 2048),
+                    (512, 256, 1024), (64, 2048, 1408), (96, 200, 1152), (257, 385, 512)]
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "i8b64"])
+@pytest.mark.parametrize("M,N,K", GEMM_INT8_SHAPES)
+def test_gemm_int8_formats(oracle, fmt, M, N, K):
+    """Against the exact product at the GEMM bar, and tightly against the
+    format's tile contract: Q8_0 multiplies RN_fp16(c d) (the fp16 tile, as
+    lq_dequant_f16), int8 block-64 keeps the codes exact and applies the fp32
+    scale to each block sum, so only fp32 accumulation error remains."""
+    say("gemm", fmt, M, N, K)
+    w, s = make(fmt, 91 + N + K, N, K)
+    X = lqgen.activations(57 + M, M * K, np.float16).reshape(M, K)
+    Wd = gu.upload(fmt, w, s, N, K)
+    Y = gu.gemm(Wd, X, M, N, K, fmt)
+    Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K)
+    assert gu.ratio(Y, Yr, S, gu.GEMM_REL, gu.GEMM_ABS) <= 1.0
+    Yt, St = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K, round_w_f16=(fmt == "q8_0"))
+    assert gu.ratio(Y, Yt, St, 1e-4, 1e-6) <= 1.0
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "i8b64"])
+def test_gemm_int8_one_hot_rows(fmt):
+    """X[m] = e_{k_m}: Q8_0 gives Y[m, :] = RN_fp16 of weight column k_m and
+    int8 block-64 gives RN_fp32 of it (lq_dequant_f16 / lq_dequant_f32), bit
+    for bit."""
+    M, N, K = 72, 160, 384
+    say("gemm one-hot", fmt, M, N, K)
+    w, s = make(fmt, 6, N, K)
+    Wd = gu.upload(fmt, w, s, N, K)
+    ks = [(11 * m + 5) % K for m in range(M)]
+    X = np.zeros((M, K), np.float16)
+    for m, k in enumerate(ks):
+        X[m, k] = 1
+    Y = gu.gemm(Wd, X, M, N, K, fmt)
+    if fmt == "q8_0":
+        out = torch.empty(N * K, dtype=torch.uint16, device="cuda")
+        lq.lq_dequant_f16(gu.FMT[fmt], Wd, out, N, K)
+        torch.cuda.synchronize()
+        ref = out.cpu().numpy().reshape(N, K).view(np.float16).astype(np.float32)
+    else:
+        out = torch.empty(N * K, dtype=torch.float32, device="cuda")
+        lq.lq_dequant_f32(gu.FMT[fmt], Wd, out, N, K)
+        torch.cuda.synchronize()
+        ref = out.cpu().numpy().reshape(N, K)
+    for m, k in enumerate(ks):
+        assert np.array_equal(Y[m].view(np.uint32), ref[:, k].view(np.uint32)), m
+
+
 def test_gemm_one_hot_rows_pin_tile():
     """X[m] = e_{k_m} gives Y[m, :] = RN_fp16 of weight column k_m, bit for bit."""
     M, N, K = 40, 160, 320
@@ -420,6 +472,26 @@ def test_matmul_routes_by_token_count():
     lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(x), Y, 1, N, K)
     torch.cuda.synchronize()
     assert np.array_equal(Y[:N].cpu().numpy(), y1)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["q8_0", "i8b64"])
+def test_workload_int8_prefill(oracle, fmt):
+    """The prefill FFN shapes (2048 / 11008, M = 512) with int8 weights:
+    sampled outputs against the exact product at the GEMM bar."""
+    M = 512
+    for name, N, K in (("gate", 11008, 2048), ("down", 2048, 11008)):
+        say("gemm workload", fmt, name, M, N, K)
+        w, s = make(fmt, 4400 + N, N, K)
+        X = lqgen.activations(4500 + K, M * K, np.float16).reshape(M, K)
+        Wd = gu.upload(fmt, w, s, N, K)
+        Y = gu.gemm(Wd, X, M, N, K, fmt)
+        rng = np.random.default_rng(N + K)
+        ms = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 511], rng.integers(0, M, 25)]))
+        ns = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, N - 1], rng.integers(0, N, 120)]))
+        Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K, ms=ms, ns=ns)
+        r = gu.ratio(Y[np.ix_(ms, ns)], Yr, S, gu.GEMM_REL, gu.GEMM_ABS)
+        assert r <= 1.0, (fmt, name, r)
 
 
 @pytest.mark.slow
