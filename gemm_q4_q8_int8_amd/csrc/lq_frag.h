@@ -54,9 +54,9 @@ __device__ __forceinline__ half8_t q4_frag(uint32_t d) {
     return __builtin_bit_cast(half8_t, u32x4{as_u32(a), as_u32(b), as_u32(c), as_u32(f)});
 }
 
-// B fragment of int8 codes: dword lo holds elements 4j..4j+3, dword hi the
-// elements 16 further on, in element order.  Flipping each sign bit gives
-// c + 128; a byte permute places two of those under 0x64 (fp16 1024 + v) and
+// B fragment of 8 int8 codes (the 4 bytes of `lo`, then the 4 of `hi`) as
+// exact fp16 values in that order.  Flipping each sign bit gives c + 128; a
+// byte permute places two of those under 0x64 (fp16 1024 + v) and
 // subtracting 1152 leaves the exact codes.
 __device__ __forceinline__ half8_t i8_frag(uint32_t lo, uint32_t hi) {
     const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};

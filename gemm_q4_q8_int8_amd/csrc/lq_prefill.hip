@@ -155,16 +155,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
         else __builtin_amdgcn_global_load_lds(ssrc, sdst, 4, 0, 0);
     };
 
-    // Fragment offsets inside a slot.  A fragment of token group q, lane
-    // (t, j): elements 4j..4j+3 (bytes 8j, logical chunk j / 2) and 16+4j ..
-    // (bytes 32 + 8j, chunk 2 + j / 2) of token 16 q + t.
+    // Fragment offsets inside a slot.  Q4_0, token group q, lane (t, j):
+    // elements 4j..4j+3 (bytes 8j, logical chunk j / 2) and 16+4j .. (bytes
+    // 32 + 8j, chunk 2 + j / 2) of token 16 q + t, matching the nibbles of
+    // code dword j.  int8: elements 8j .. 8j+7, i.e. logical chunk j, one
+    // 16-byte read (16 tokens x one chunk: conflict-free under the swizzle).
     uint32_t xoff[NT][2];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
         const int tok = 16 * q + r;
         const int sw = (tok >> 2) & 3;
-        xoff[q][0] = uint32_t(C::XOFF + tok * 64 + ((g >> 1) ^ sw) * 16 + 8 * (g & 1));
-        xoff[q][1] = uint32_t(C::XOFF + tok * 64 + ((2 + (g >> 1)) ^ sw) * 16 + 8 * (g & 1));
+        if constexpr (FMT == kQ4_0) {
+            xoff[q][0] = uint32_t(C::XOFF + tok * 64 + ((g >> 1) ^ sw) * 16 + 8 * (g & 1));
+            xoff[q][1] = uint32_t(C::XOFF + tok * 64 + ((2 + (g >> 1)) ^ sw) * 16 + 8 * (g & 1));
+        } else {
+            xoff[q][0] = uint32_t(C::XOFF + tok * 64 + (g ^ sw) * 16);
+            xoff[q][1] = 0;
+        }
     }
     const uint32_t woff = uint32_t(C::WOFF + w * C::PS * 1024 + 16 * lane);
     const uint32_t soff = uint32_t(C::SOFF + w * 256 + 16 * r);
@@ -187,15 +194,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
         lds_barrier();
         issue(min(st + C::STAGES - 1, nst - 1));
         const uint8_t* slot = slot_of(st);
+        // c[0]: Q4_0 code dwords (lane (r, j), slot m: dword j of row 4r + m).
+        // int8: c[0] / c[1] hold bytes 8j .. 8j+3 / 8j+4 .. 8j+7 of the
+        // step's 32 codes of row 4r + m (a transpose of double dwords).
         u32x4 c[C::PS];
-#pragma unroll
-        for (int p = 0; p < C::PS; ++p) c[p] = xpose(*reinterpret_cast<const u32x4*>(slot + woff + p * 1024));
-        const u32x4 sc = *reinterpret_cast<const u32x4*>(slot + soff);
         half8_t xa[NT];
+        if constexpr (FMT == kQ4_0) {
+            c[0] = xpose(*reinterpret_cast<const u32x4*>(slot + woff));
 #pragma unroll
-        for (int q = 0; q < NT; ++q)
-            xa[q] = x_frag<FMT>(*reinterpret_cast<const u32x2*>(slot + xoff[q][0]),
-                                *reinterpret_cast<const u32x2*>(slot + xoff[q][1]));
+            for (int q = 0; q < NT; ++q)
+                xa[q] = x_frag<FMT>(*reinterpret_cast<const u32x2*>(slot + xoff[q][0]),
+                                    *reinterpret_cast<const u32x2*>(slot + xoff[q][1]));
+        } else {
+            const u32x4 p0 = *reinterpret_cast<const u32x4*>(slot + woff);
+            const u32x4 p1 = *reinterpret_cast<const u32x4*>(slot + woff + 1024);
+            c[0] = xpose(u32x4{p0.x, p0.z, p1.x, p1.z});
+            c[1] = xpose(u32x4{p0.y, p0.w, p1.y, p1.w});
+#pragma unroll
+            for (int q = 0; q < NT; ++q) xa[q] = *reinterpret_cast<const half8_t*>(slot + xoff[q][0]);
+        }
+        const u32x4 sc = *reinterpret_cast<const u32x4*>(slot + soff);
         const uint32_t sv[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
                 const half8_t dd = {d, d, d, d, d, d, d, d};
                 half8_t wb;
                 if constexpr (FMT == kQ4_0) wb = q4_frag(c[0][m]) * dd;
-                else wb = i8_frag(c[0][m], c[C::PS - 1][m]) * dd;
+                else wb = i8_frag(c[0][m], c[C::PS - 1][m]) * dd;   // PS == 2 here
 #pragma unroll
                 for (int q = 0; q < NT; ++q)
                     acc[q][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[q], wb, acc[q][m], 0, 0, 0);
