@@ -401,7 +401,8 @@ lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, 
 }
 
 namespace {
-bool use_lds_tile_gemm(int32_t fmt) { return fmt == LQ_Q4_0 && !LQ_GEMM_Q4_PREFILL; }
+// Q4_0: the LDS-tile GEMM; Q8_0 and int8 block-64: the register-fragment one.
+bool use_lds_tile_gemm(int32_t fmt) { return fmt == LQ_Q4_0; }
 
 size_t gemm_ws(int32_t fmt, int64_t M, int64_t N, int64_t K) {
     return use_lds_tile_gemm(fmt) ? lq::gemm_workspace_bytes(M, N, K) : lq::prefill_workspace_bytes(M, N, K);

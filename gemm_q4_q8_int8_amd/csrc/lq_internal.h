@@ -161,16 +161,10 @@ hipError_t launch_gemm_q4_0(const void* W, const void* X, float* Y, int64_t M, i
 // Y = sum of S partial M x N slices (slice order), for split-K GEMMs.
 hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipStream_t stream);
 
-// Prefill GEMM for every format (weights straight from the packed layout
-// into matrix-core operands).
+// Prefill GEMM for Q8_0 and int8 block-64 (codes straight from the packed
+// layout into matrix-core operands).
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prefill(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t N,
                           int64_t K, void* ws, hipStream_t stream);
-
-// Q4_0 prefill: 1 = the register-fragment kernel (launch_prefill), 0 = the
-// LDS-tile kernel (launch_gemm_q4_0).
-#ifndef LQ_GEMM_Q4_PREFILL
-#define LQ_GEMM_Q4_PREFILL 0
-#endif
 
 }  // namespace lq

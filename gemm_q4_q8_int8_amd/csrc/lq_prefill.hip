@@ -1,6 +1,6 @@
-// Prefill GEMM for all three weight formats: Y[M x N] = X[M x K] W[N x K]^T,
-// fp16 X, weights read straight from the packed layout into matrix-core
-// operands.
+// Prefill GEMM for int8-coded weights (Q8_0 and int8 block-64):
+// Y[M x N] = X[M x K] W[N x K]^T, fp16 X, weights read straight from the
+// packed layout into matrix-core operands.
 //
 // Prefill is compute bound ("oxinfer" page, "Performance"); the page's GPU
 // kernels dequantize the weight tile on chip before a dense tile product
@@ -17,19 +17,23 @@
 //     are free of bank conflicts), the raw code bytes of the 4 tiles and
 //     their scales.  Each wave copies its own tile's codes and a quarter of
 //     the activations; one barrier per step.
-//   * Each wave reads its tile's codes for the step (one 16-byte LDS read per
-//     part, lane (r, g) holding tile row 4r + g), transposes them across the
-//     four 16-lane rows with permlane swaps so that lane (r, j) holds k-set j
-//     of rows 4r .. 4r+3, and turns them into fp16 B fragments in registers.
-//     The four waves share the activation fragments of the slot.
-//   * Q4_0 and Q8_0: the B fragment is RN_fp16(code * d) (exact fp16 code,
-//     one fp16 multiply by the fp16 scale), the same fp16 tile contract as
-//     lq_dequant_f16, and the 16 matrix instructions of a step accumulate
-//     straight into the fp32 tile.  int8 block-64: the fp32 scale is not an
-//     fp16 value, so the codes stay exact and the scale is applied in fp32
-//     to each step's block sums (more accurate than an fp16 tile).
+//   * Each wave reads its tile's codes for the step (two 16-byte LDS reads,
+//     lane (r, g) holding tile row 4r + g), transposes them across the four
+//     16-lane rows with permlane swaps (as double dwords) so that lane (r, j)
+//     holds codes 8j .. 8j+7 of rows 4r .. 4r+3, and turns them into fp16 B
+//     fragments in registers.  Its activation fragment is one 16-byte read
+//     of elements 8j .. 8j+7; the four waves share the slot's activations.
+//   * Q8_0: the B fragment is RN_fp16(c d) (exact fp16 code, one fp16
+//     multiply by the fp16 scale), the fp16 tile contract of lq_dequant_f16,
+//     and the 16 matrix instructions of a step accumulate straight into the
+//     fp32 tile.  int8 block-64: the fp32 scale is not an fp16 value, so the
+//     codes stay exact and the scale is applied in fp32 to each step's
+//     block sums (more accurate than an fp16 tile).
 //   * Short K slices per output tile split K across workgroups into the
 //     caller's workspace; a second kernel adds the slices in order.
+//   * Q4_0 weights use the LDS-tile GEMM: this design was measured on them
+//     too (nibbles selected per lane group) and was slower on the 11008-row
+//     matrices (474 against 547 TFLOP/s).
 #include "lq_frag.h"
 
 #include <algorithm>
@@ -54,12 +58,12 @@ constexpr int kTok = 16 * NT;
 // copy to LDS fills a zero-extended dword).
 template <int FMT>
 struct Cfg {
-    static constexpr int PS = FMT == kQ4_0 ? 1 : 2;   // 16-byte code parts per step
+    static constexpr int PS = 2;                       // 16-byte code parts per step
     static constexpr int XOFF = 0;
     static constexpr int WOFF = kTok * 64;             // 64 bytes per token
     static constexpr int SOFF = WOFF + kWaves * PS * 1024;
     static constexpr int SLOT = SOFF + kWaves * 256;
-    static constexpr int STAGES = NT == 4 ? (FMT == kQ4_0 ? 8 : 6) : (FMT == kQ4_0 ? 6 : 4);
+    static constexpr int STAGES = NT == 4 ? 6 : 4;
     static constexpr int LDS = STAGES * SLOT;         // at most 80 KB: two workgroups per CU
     static constexpr int XL = NT / 4;                 // activation copies per wave per step
     static constexpr int LOADS = XL + PS + 1;          // copies per wave per step
@@ -155,23 +159,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
         else __builtin_amdgcn_global_load_lds(ssrc, sdst, 4, 0, 0);
     };
 
-    // Fragment offsets inside a slot.  Q4_0, token group q, lane (t, j):
-    // elements 4j..4j+3 (bytes 8j, logical chunk j / 2) and 16+4j .. (bytes
-    // 32 + 8j, chunk 2 + j / 2) of token 16 q + t, matching the nibbles of
-    // code dword j.  int8: elements 8j .. 8j+7, i.e. logical chunk j, one
-    // 16-byte read (16 tokens x one chunk: conflict-free under the swizzle).
-    uint32_t xoff[NT][2];
+    // Fragment offsets inside a slot: token group q, lane (t, j) takes
+    // elements 8j .. 8j+7 of token 16 q + t, i.e. logical chunk j, one 16-byte
+    // read (16 tokens x one chunk: conflict-free under the swizzle).
+    uint32_t xoff[NT];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
         const int tok = 16 * q + r;
         const int sw = (tok >> 2) & 3;
-        if constexpr (FMT == kQ4_0) {
-            xoff[q][0] = uint32_t(C::XOFF + tok * 64 + ((g >> 1) ^ sw) * 16 + 8 * (g & 1));
-            xoff[q][1] = uint32_t(C::XOFF + tok * 64 + ((2 + (g >> 1)) ^ sw) * 16 + 8 * (g & 1));
-        } else {
-            xoff[q][0] = uint32_t(C::XOFF + tok * 64 + (g ^ sw) * 16);
-            xoff[q][1] = 0;
-        }
+        xoff[q] = uint32_t(C::XOFF + tok * 64 + (g ^ sw) * 16);
     }
     const uint32_t woff = uint32_t(C::WOFF + w * C::PS * 1024 + 16 * lane);
     const uint32_t soff = uint32_t(C::SOFF + w * 256 + 16 * r);
@@ -194,25 +190,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
         lds_barrier();
         issue(min(st + C::STAGES - 1, nst - 1));
         const uint8_t* slot = slot_of(st);
-        // c[0]: Q4_0 code dwords (lane (r, j), slot m: dword j of row 4r + m).
-        // int8: c[0] / c[1] hold bytes 8j .. 8j+3 / 8j+4 .. 8j+7 of the
-        // step's 32 codes of row 4r + m (a transpose of double dwords).
-        u32x4 c[C::PS];
+        // Lane (r, j), slot m: the codes of elements 8j .. 8j+7 of row 4r + m
+        // in c[0] (first four) and c[1] (last four), by a transpose of double
+        // dwords.
+        u32x4 c[2];
         half8_t xa[NT];
-        if constexpr (FMT == kQ4_0) {
-            c[0] = xpose(*reinterpret_cast<const u32x4*>(slot + woff));
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(slot + woff);
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(slot + woff + 1024);
+        c[0] = xpose(u32x4{p0.x, p0.z, p1.x, p1.z});
+        c[1] = xpose(u32x4{p0.y, p0.w, p1.y, p1.w});
 #pragma unroll
-            for (int q = 0; q < NT; ++q)
-                xa[q] = x_frag<FMT>(*reinterpret_cast<const u32x2*>(slot + xoff[q][0]),
-                                    *reinterpret_cast<const u32x2*>(slot + xoff[q][1]));
-        } else {
-            const u32x4 p0 = *reinterpret_cast<const u32x4*>(slot + woff);
-            const u32x4 p1 = *reinterpret_cast<const u32x4*>(slot + woff + 1024);
-            c[0] = xpose(u32x4{p0.x, p0.z, p1.x, p1.z});
-            c[1] = xpose(u32x4{p0.y, p0.w, p1.y, p1.w});
-#pragma unroll
-            for (int q = 0; q < NT; ++q) xa[q] = *reinterpret_cast<const half8_t*>(slot + xoff[q][0]);
-        }
+        for (int q = 0; q < NT; ++q) xa[q] = *reinterpret_cast<const half8_t*>(slot + xoff[q]);
         const u32x4 sc = *reinterpret_cast<const u32x4*>(slot + soff);
         const uint32_t sv[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
@@ -228,9 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(const PrefillArgs 
             } else {
                 const _Float16 d = __builtin_bit_cast(_Float16, uint16_t(sv[m]));
                 const half8_t dd = {d, d, d, d, d, d, d, d};
-                half8_t wb;
-                if constexpr (FMT == kQ4_0) wb = q4_frag(c[0][m]) * dd;
-                else wb = i8_frag(c[0][m], c[C::PS - 1][m]) * dd;   // PS == 2 here
+                const half8_t wb = i8_frag(c[0][m], c[1][m]) * dd;
 #pragma unroll
                 for (int q = 0; q < NT; ++q)
                     acc[q][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[q], wb, acc[q][m], 0, 0, 0);
@@ -340,7 +326,6 @@ hipError_t launch_prefill(int fmt, const void* W, const void* X, float* Y, int64
     a.vec = (N % 4 == 0 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0) ? 1 : 0;
     hipError_t e;
     switch (fmt) {
-        case kQ4_0: e = launch_fmt<kQ4_0>(a, grid, stream); break;
         case kQ8_0: e = launch_fmt<kQ8_0>(a, grid, stream); break;
         case kI8B64: e = launch_fmt<kI8B64>(a, grid, stream); break;
         default: return hipErrorInvalidValue;
