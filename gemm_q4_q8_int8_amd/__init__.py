@@ -16,12 +16,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblq.so")
 
 LQ_Q4_0, LQ_Q8_0, LQ_I8B64 = 0, 1, 2
-LQ_F32, LQ_F16 = 0, 1
+LQ_F32, LQ_F16, LQ_BF16 = 0, 1, 2
 FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64}
 
 # Every symbol include/lq.h declares.
 EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq_scale_offset",
-           "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_dequant_f32",
+           "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_quantize", "lq_dequant_f32",
            "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi", "lq_gemv_multi_batch",
            "lq_gemm_workspace_bytes",
            "lq_gemm",
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH):
         "lq_gguf_bytes": ([i32, i64, i64], sz),
         "lq_repack_gguf": ([i32, vp, vp, i64, i64, vp], i32),
         "lq_pack_planes": ([i32, vp, vp, vp, i64, i64, vp], i32),
+        "lq_quantize": ([i32, vp, i32, vp, i64, i64, vp], i32),
         "lq_dequant_f32": ([i32, vp, vp, i64, i64, vp], i32),
         "lq_dequant_f16": ([i32, vp, vp, i64, i64, vp], i32),
         "lq_gemv": ([i32, vp, vp, i32, vp, i64, i64, vp], i32),
@@ -177,6 +178,14 @@ def lq_repack_gguf(fmt, src, dst, N, K, stream=None):
 def lq_pack_planes(fmt, codes, scales, dst, N, K, stream=None):
     _check(load().lq_pack_planes(_fmt(fmt), _ptr(codes), _ptr(scales), _ptr(dst), N, K,
                                  _stream(stream)))
+
+
+def lq_quantize(fmt, src, W, N, K, stream=None, sdt=None):
+    """src: float32 / float16 / bfloat16 tensor (N x K row-major)."""
+    if sdt is None:
+        import torch
+        sdt = LQ_BF16 if src.dtype == torch.bfloat16 else _xdt(src)
+    _check(load().lq_quantize(_fmt(fmt), _ptr(src), sdt, _ptr(W), N, K, _stream(stream)))
 
 
 def lq_dequant_f32(fmt, W, out, N, K, stream=None):

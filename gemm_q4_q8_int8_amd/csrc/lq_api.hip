@@ -303,6 +303,17 @@ lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales, voi
     return e == hipSuccess ? LQ_OK : hip_fail(e, "pack launch");
 }
 
+lq_status lq_quantize(int32_t fmt, const void* src, int32_t sdt, void* W, int64_t N, int64_t K,
+                      void* stream) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    if (sdt != LQ_F32 && sdt != LQ_F16 && sdt != LQ_BF16)
+        return fail(LQ_ERR_DTYPE, "unknown source dtype %d", sdt);
+    LQ_TRY(check_ptr(src, 16, "src"));
+    LQ_TRY(check_ptr(W, 16, "W"));
+    const hipError_t e = lq::launch_quantize(fmt, sdt, src, W, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "quantize launch");
+}
+
 static lq_status dequant_common(int32_t fmt, const void* W, void* out, int64_t N, int64_t K,
                                 void* stream, bool f16) {
     LQ_TRY(check_fmt_shape(fmt, N, K));

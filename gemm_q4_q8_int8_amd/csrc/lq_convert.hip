@@ -15,7 +15,10 @@
 //   bits, so it is rounded to fp16 in integer arithmetic (one rounding, round
 //   to nearest even, gradual underflow) rather than through fp32.
 //
-// One thread handles one block (repack, pack) or 32 weights (dequant).  These kernels run once per weight
+//   quantize: fp32 / fp16 / bf16 row-major weights -> the packed layout
+//   (load-time block quantization; the rule is stated at quantize_kernel).
+//
+// One thread handles one block (repack, pack, quantize) or 32 weights (dequant).  These kernels run once per weight
 // upload or inside tests; they are not on the timed decode path.
 #include "lq_internal.h"
 
@@ -183,6 +186,107 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     }
 }
 
+// ------------------------------------------------------------ quantize ----
+// Load-time block quantization ("oxinfer" page, "How it works": weights are
+// block-quantized at load time; "wgpu-llm" page, "INT8 mode": symmetric int8
+// with block size 64).  The pages give no rounding rule; the one implemented,
+// step by step in IEEE fp32 (correctly rounded divisions, round to nearest
+// even):
+//   Q8_0:  a = max |w|, d = fp16(a / 127), c = clamp(rint(w / d), -127, 127)
+//   Q4_0:  m = first w of largest |w|, d = fp16(m / -8),
+//          q = clamp(rint(w / d), -8, 7) + 8
+//   int8 block-64: a = max |w|, s = a / 127, c = clamp(rint(w / s), -127, 127)
+// A zero scale gives zero weights (code 0, Q4_0 code 8).  One thread per
+// block, written straight into the packed tiled layout.
+template <int SDT>
+__device__ __forceinline__ float source_value(const void* src, int64_t i) {
+    if constexpr (SDT == kF32) {
+        return static_cast<const float*>(src)[i];
+    } else if constexpr (SDT == kF16) {
+        return float(static_cast<const _Float16*>(src)[i]);
+    } else {
+        return __uint_as_float(uint32_t(static_cast<const uint16_t*>(src)[i]) << 16);   // bf16
+    }
+}
+
+// fp16(v) of an fp32 value that is first materialized as fp32: without the
+// empty asm the compiler folds x / -8 and the conversion into one
+// v_fma_mixlo_f16(x, -0.125, +0), which turns a -0 quotient into +0.
+__device__ __forceinline__ _Float16 to_half(float v) {
+    asm volatile("" : "+v"(v));
+    return _Float16(v);
+}
+
+__device__ __forceinline__ int round_clamp(float v, int lo, int hi) {
+    return int(fminf(fmaxf(rintf(v), float(lo)), float(hi)));
+}
+
+template <int FMT, int SDT>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restrict__ src,
+                                                            uint8_t* __restrict__ dst, int64_t N,
+                                                            int64_t nu, size_t scale_off) {
+    constexpr int E = unit_elems(FMT);
+    constexpr int P = unit_parts(FMT);
+    const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (g >= N * nu) return;
+    const int64_t row = g / nu;
+    const int64_t u = g - row * nu;
+    const int64_t K = nu * E;
+    float w[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[e] = source_value<SDT>(src, row * K + u * E + e);
+    const TiledPos pos = tiled_pos(FMT, N, nu, row, u);
+    uint8_t q[E];
+    if constexpr (FMT == kI8B64) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fabsf(w[e]) > a ? fabsf(w[e]) : a;
+        const float s = a / 127.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) q[e] = uint8_t(int8_t(s == 0.0f ? 0 : round_clamp(w[e] / s, -127, 127)));
+        reinterpret_cast<float*>(dst + scale_off)[pos.scale] = s;
+    } else {
+        _Float16 dh;
+        if constexpr (FMT == kQ8_0) {
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) a = fabsf(w[e]) > a ? fabsf(w[e]) : a;
+            dh = to_half(a / 127.0f);
+        } else {
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = fabsf(w[e]) > fabsf(m) ? w[e] : m;
+            dh = to_half(m / -8.0f);
+        }
+        const float d = float(dh);
+        if constexpr (FMT == kQ8_0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) q[e] = uint8_t(int8_t(d == 0.0f ? 0 : round_clamp(w[e] / d, -127, 127)));
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) q[e] = uint8_t(d == 0.0f ? 8 : round_clamp(w[e] / d, -8, 7) + 8);
+        }
+        reinterpret_cast<_Float16*>(dst + scale_off)[pos.scale] = dh;
+    }
+    // Codes: Q4_0 byte j = q_j | q_{j+16} << 4 (GGUF order); int8: bytes in order.
+    uint32_t b[4 * P];
+    if constexpr (FMT == kQ4_0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            b[i] = uint32_t(q[4 * i] | (q[4 * i + 16] << 4)) | (uint32_t(q[4 * i + 1] | (q[4 * i + 17] << 4)) << 8) |
+                   (uint32_t(q[4 * i + 2] | (q[4 * i + 18] << 4)) << 16) | (uint32_t(q[4 * i + 3] | (q[4 * i + 19] << 4)) << 24);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4 * P; ++i)
+            b[i] = uint32_t(q[4 * i]) | (uint32_t(q[4 * i + 1]) << 8) | (uint32_t(q[4 * i + 2]) << 16) |
+                   (uint32_t(q[4 * i + 3]) << 24);
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        *reinterpret_cast<u32x4*>(dst + pos.code + size_t(p) * pos.part_stride) =
+            u32x4{b[4 * p], b[4 * p + 1], b[4 * p + 2], b[4 * p + 3]};
+}
+
 int blocks_for(int64_t n) { return int((n + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -217,6 +321,29 @@ hipError_t launch_pack_planes(int fmt, const void* codes, const void* scales, vo
         case kI8B64: hipLaunchKernelGGL(pack_kernel<kI8B64>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(int fmt, int sdt, const void* src, void* dst, int64_t N, int64_t K,
+                           hipStream_t stream) {
+    const int64_t nu = K / unit_elems(fmt);
+    const size_t off = align256(code_plane_bytes(fmt, N, K));
+    uint8_t* d = static_cast<uint8_t*>(dst);
+    const dim3 grid(blocks_for(N * nu)), block(kThreads);
+#define LQ_QK(F, S) hipLaunchKernelGGL((quantize_kernel<F, S>), grid, block, 0, stream, src, d, N, nu, off)
+    switch (fmt * 3 + sdt) {
+        case kQ4_0 * 3 + kF32: LQ_QK(kQ4_0, kF32); break;
+        case kQ4_0 * 3 + kF16: LQ_QK(kQ4_0, kF16); break;
+        case kQ4_0 * 3 + kBF16: LQ_QK(kQ4_0, kBF16); break;
+        case kQ8_0 * 3 + kF32: LQ_QK(kQ8_0, kF32); break;
+        case kQ8_0 * 3 + kF16: LQ_QK(kQ8_0, kF16); break;
+        case kQ8_0 * 3 + kBF16: LQ_QK(kQ8_0, kBF16); break;
+        case kI8B64 * 3 + kF32: LQ_QK(kI8B64, kF32); break;
+        case kI8B64 * 3 + kF16: LQ_QK(kI8B64, kF16); break;
+        case kI8B64 * 3 + kBF16: LQ_QK(kI8B64, kBF16); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef LQ_QK
     return hipGetLastError();
 }
 

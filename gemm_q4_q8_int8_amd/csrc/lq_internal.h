@@ -10,7 +10,7 @@
 namespace lq {
 
 enum Fmt : int { kQ4_0 = 0, kQ8_0 = 1, kI8B64 = 2 };
-enum XType : int { kF32 = 0, kF16 = 1 };
+enum XType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // ------------------------------------------------------ packed layout ----
 // Rows are grouped in tiles of 64.  A "unit" is one scale block of a row
@@ -150,6 +150,8 @@ hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, in
                               hipStream_t stream);
 hipError_t launch_pack_planes(int fmt, const void* codes, const void* scales, void* dst, int64_t N,
                               int64_t K, hipStream_t stream);
+hipError_t launch_quantize(int fmt, int sdt, const void* src, void* dst, int64_t N, int64_t K,
+                           hipStream_t stream);
 hipError_t launch_dequant(int fmt, bool to_f16, const void* W, void* out, int64_t N,
                           int64_t K, hipStream_t stream);
 

@@ -84,10 +84,12 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 3
+#define LQ_ABI_VERSION 4
 
 typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2 } lq_fmt;
-typedef enum lq_dtype { LQ_F32 = 0, LQ_F16 = 1 } lq_dtype;
+/* Activation and source dtypes.  LQ_BF16 is accepted only as the source of
+ * lq_quantize. */
+typedef enum lq_dtype { LQ_F32 = 0, LQ_F16 = 1, LQ_BF16 = 2 } lq_dtype;
 
 typedef enum lq_status {
     LQ_OK = 0,
@@ -151,6 +153,23 @@ lq_status lq_dequant_f32(int32_t fmt, const void* W, float* out,
  * This is the tile contract of lq_gemm.  out: N*K uint16, 16-byte aligned. */
 lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out,
                          int64_t N, int64_t K, void* stream);
+
+/* Load-time block quantization ("oxinfer" page, "How it works": weights are
+ * block-quantized at load time; "wgpu-llm" page, "INT8 mode": symmetric int8
+ * with block size 64) of a row-major N x K matrix into the packed layout.
+ * src: N*K finite values of dtype sdt (LQ_F32, LQ_F16 or LQ_BF16), 16-byte
+ * aligned; W: lq_packed_bytes(fmt, N, K) bytes, 16-byte aligned.  The pages
+ * give no rounding rule; this one, in IEEE fp32 steps (divisions correctly
+ * rounded, rint = round to nearest, ties to even), per block:
+ *   LQ_Q8_0:  a = max |w|; d = fp16(a / 127); c = clamp(rint(w / d), -127, 127)
+ *   LQ_Q4_0:  m = the first w of largest |w|; d = fp16(m / -8);
+ *             q = clamp(rint(w / d), -8, 7) + 8  (m itself becomes code 0)
+ *   LQ_I8B64: a = max |w|; s = a / 127 (fp32);   c = clamp(rint(w / s), -127, 127)
+ * A zero scale gives zero weights.  Non-finite inputs give unspecified codes.
+ * lq_dequant_f32 of the result is within |d| / 2 of w per element (|d| for
+ * Q4_0 codes clamped at 15). */
+lq_status lq_quantize(int32_t fmt, const void* src, int32_t sdt, void* W,
+                      int64_t N, int64_t K, void* stream);
 
 /* Decode GEMV: y[n] = sum_k w[n,k] * x[k] for n < N, accumulated in fp32 with
  * the weights decoded exactly.  W: packed N x K; x: K values of dtype xdt;

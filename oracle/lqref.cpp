@@ -249,6 +249,74 @@ int lqref_unpack_gguf(int fmt, const uint8_t* aos, int64_t N, int64_t K,
     return 0;
 }
 
+// Source element i as a float (exact for all three source types).
+static float source_at(const void* src, int sdt, int64_t i) {
+    if (sdt == LQREF_F32) return static_cast<const float*>(src)[i];
+    const uint16_t h = static_cast<const uint16_t*>(src)[i];
+    if (sdt == LQREF_F16) return static_cast<float>(half_to_double(h));
+    uint32_t bits = uint32_t(h) << 16;   // bf16 is the top half of an fp32
+    float f;
+    std::memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+// Round to the nearest integer, ties to even, then clamp (the value is finite).
+static int round_clamp(float v, int lo, int hi) {
+    const float r = std::nearbyint(v);   // default rounding mode: nearest even
+    if (r < float(lo)) return lo;
+    if (r > float(hi)) return hi;
+    return int(r);
+}
+
+int lqref_quantize(int fmt, const void* src, int sdt, int64_t N, int64_t K,
+                   uint8_t* out, float* scales) {
+    if (!shape_ok(fmt, N, K) || !src || !out) return -1;
+    if (sdt != LQREF_F32 && sdt != LQREF_F16 && sdt != LQREF_BF16) return -1;
+    if (fmt == LQREF_I8B64 && !scales) return -1;
+    const int E = block_elems(fmt);
+    const int64_t nb = K / E;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float w[64];
+            for (int e = 0; e < E; ++e) w[e] = source_at(src, sdt, n * K + b * E + e);
+            if (fmt == LQREF_I8B64) {
+                float a = 0.0f;
+                for (int e = 0; e < E; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;
+                const float s = a / 127.0f;
+                scales[n * nb + b] = s;
+                int8_t* c = reinterpret_cast<int8_t*>(out) + n * K + b * E;
+                for (int e = 0; e < E; ++e) c[e] = int8_t(s == 0.0f ? 0 : round_clamp(w[e] / s, -127, 127));
+                continue;
+            }
+            uint8_t* blk = out + (n * nb + b) * gguf_block_bytes(fmt);
+            uint16_t d16;
+            if (fmt == LQREF_Q8_0) {
+                float a = 0.0f;
+                for (int e = 0; e < 32; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;
+                d16 = double_to_half(double(a / 127.0f));
+            } else {
+                float m = 0.0f;   // first element of largest magnitude, with its sign
+                for (int e = 0; e < 32; ++e) m = std::fabs(w[e]) > std::fabs(m) ? w[e] : m;
+                d16 = double_to_half(double(m / -8.0f));
+            }
+            blk[0] = uint8_t(d16 & 0xFF);
+            blk[1] = uint8_t(d16 >> 8);
+            const float d = float(half_to_double(d16));
+            int q[32];
+            for (int e = 0; e < 32; ++e) {
+                if (fmt == LQREF_Q8_0) q[e] = d == 0.0f ? 0 : round_clamp(w[e] / d, -127, 127);
+                else q[e] = d == 0.0f ? 8 : round_clamp(w[e] / d, -8, 7) + 8;
+            }
+            if (fmt == LQREF_Q8_0) {
+                for (int j = 0; j < 32; ++j) blk[2 + j] = uint8_t(int8_t(q[j]));
+            } else {
+                for (int j = 0; j < 16; ++j) blk[2 + j] = uint8_t(q[j] | (q[j + 16] << 4));
+            }
+        }
+    }
+    return 0;
+}
+
 int lqref_gemv(int fmt, const uint8_t* w, const void* scales, const void* x,
                int xdt, int64_t N, int64_t K, const int64_t* rows, int64_t nrows,
                double* y, double* S, int nthreads) {

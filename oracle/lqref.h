@@ -29,7 +29,7 @@ extern "C" {
 #endif
 
 enum { LQREF_Q4_0 = 0, LQREF_Q8_0 = 1, LQREF_I8B64 = 2 };
-enum { LQREF_F32 = 0, LQREF_F16 = 1 };
+enum { LQREF_F32 = 0, LQREF_F16 = 1, LQREF_BF16 = 2 };
 
 /* IEEE binary16 decode (exact in double) and round-to-nearest-even encode. */
 double   lqref_half_to_double(uint16_t h);
@@ -57,6 +57,23 @@ int lqref_pack_gguf(int fmt, const int8_t* codes, const uint16_t* scales,
                     int64_t N, int64_t K, uint8_t* out);
 int lqref_unpack_gguf(int fmt, const uint8_t* aos, int64_t N, int64_t K,
                       int8_t* codes, uint16_t* scales);
+
+/* Load-time quantization of a row-major N x K matrix ("oxinfer" page, "How
+ * it works": block quantization of weights at load time; "wgpu-llm" page,
+ * "INT8 mode": symmetric int8, block size 64).  The pages give no rounding
+ * rule; the reading implemented here, in IEEE fp32 operations:
+ *   Q8_0:  a = max |w| over the 32-block; d = fp16(a / 127);
+ *          c = clamp(rint(w / float(d)), -127, 127), 0 when d == 0.
+ *   Q4_0:  m = the block's first element of largest |w|; d = fp16(m / -8);
+ *          q = clamp(rint(w / float(d)) + 8, 0, 15), 8 when d == 0.
+ *   I8B64: a = max |w| over the 64-block; s = a / 127 (fp32);
+ *          c = clamp(rint(w / s), -127, 127), 0 when s == 0.
+ * rint rounds to nearest, ties to even; fp16() rounds to nearest even.
+ * src: N*K values of dtype sdt (LQREF_F32, LQREF_F16 bits, LQREF_BF16 bits),
+ * finite.  Q4_0 / Q8_0: out = GGUF array-of-blocks bytes (scales unused);
+ * I8B64: out = N*K int8 codes and scales = N*K/64 fp32. */
+int lqref_quantize(int fmt, const void* src, int sdt, int64_t N, int64_t K,
+                   uint8_t* out, float* scales);
 
 /* y[i] = sum_k w[rows[i],k] * x[k] and S[i] = sum_k |w[rows[i],k] * x[k]|, in
  * double, k ascending.  x is fp32 (xdt LQREF_F32) or fp16 bits (LQREF_F16).

@@ -17,7 +17,7 @@ _SRC = os.path.join(_HERE, "lqref.cpp")
 _LIB = os.path.join(_HERE, "liblqref.so")
 
 Q4_0, Q8_0, I8B64 = 0, 1, 2
-F32, F16 = 0, 1
+F32, F16, BF16 = 0, 1, 2
 FMT_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0, "i8b64": I8B64}
 
 
@@ -43,6 +43,7 @@ def _bind(L):
         getattr(L, name).argtypes = [i32, vp, vp, i64, i64, vp]
     L.lqref_pack_gguf.argtypes = [i32, vp, vp, i64, i64, vp]
     L.lqref_unpack_gguf.argtypes = [i32, vp, i64, i64, vp, vp]
+    L.lqref_quantize.argtypes = [i32, vp, i32, i64, i64, vp, vp]
     L.lqref_gemv.argtypes = [i32, vp, vp, vp, i32, i64, i64, vp, i64, vp, vp, i32]
     L.lqref_gemm.argtypes = [i32, vp, vp, vp, i32, i64, i64, i64,
                              vp, i64, vp, i64, i32, vp, vp, i32]
@@ -107,6 +108,24 @@ class Oracle:
         out = np.empty(N * (K // 32) * self.gguf_block_bytes(fmt), np.uint8)
         _check(self.L.lqref_pack_gguf(fmt, _p(codes), _p(scales_bits), N, K, _p(out)), "pack_gguf")
         return out
+
+    def quantize(self, fmt, src, N, K, sdt=None):
+        """Load-time quantization of a row-major N x K matrix (see lqref.h).
+        src: float32 or float16 array, or uint16 bf16 bit patterns with
+        sdt=BF16.  Returns (GGUF bytes, None) for Q4_0 / Q8_0 and
+        (int8 codes, fp32 scales) for I8B64, the forms the other calls take."""
+        if sdt is None:
+            sdt, src = _xdt(src)
+        else:
+            src = np.ascontiguousarray(src)
+        if fmt == I8B64:
+            codes = np.empty(N * K, np.int8)
+            scales = np.empty(N * (K // 64), np.float32)
+            _check(self.L.lqref_quantize(fmt, _p(src), sdt, N, K, _p(codes), _p(scales)), "quantize")
+            return codes, scales
+        out = np.empty(N * (K // 32) * self.gguf_block_bytes(fmt), np.uint8)
+        _check(self.L.lqref_quantize(fmt, _p(src), sdt, N, K, _p(out), None), "quantize")
+        return out, None
 
     def unpack_gguf(self, fmt, aos, N, K):
         codes = np.empty((N, K), np.int8)

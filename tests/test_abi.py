@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 3
+    assert lq.lq_abi_version() == 4
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -114,6 +114,12 @@ def test_rejections_before_any_hip_call(L):
     md[1] = lq.lq_gemv_multi_desc(1, 0, A16, A16, A16, 4, 64, 32)
     assert g.lq_gemv_multi_batch(md, 2, None) == UNSUP          # fp32 activations
     assert "descriptor 1" in lq.lq_last_error()
+    # load-time quantization
+    assert g.lq_quantize(9, A16, 0, A16, 4, 64, None) == FMT
+    assert g.lq_quantize(0, A16, 3, A16, 4, 64, None) == DTYPE
+    assert g.lq_quantize(2, A16, 2, A16, 4, 96, None) == SHAPE
+    assert g.lq_quantize(1, A16 + 2, 1, A16, 4, 64, None) == ALIGN
+    assert g.lq_quantize(1, A16, 1, None, 4, 64, None) == ARG
     # conversions
     assert g.lq_repack_gguf(2, A16, A16, 4, 64, None) == FMT
     assert g.lq_repack_gguf(0, A16 + 1, A16, 4, 64, None) == ALIGN

@@ -6,6 +6,7 @@ import pytest
 
 from oracle import lqref
 from tests.test_oracle_pins import ALL_PINS
+from tests.test_oracle_quant import QUANT_PINS
 
 MUTANTS = {
     # nibble order (2j, 2j+1) instead of (j, j+16)
@@ -32,6 +33,19 @@ MUTANTS = {
     "ties_up": ("return (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
     # GEMM ignores the fp16 tile rounding flag
     "gemm_no_f16_round": ("if (round_w_f16)", "if (false && round_w_f16)"),
+    # quantizer: ties rounded away from zero instead of to even
+    "quant_round_away": ("const float r = std::nearbyint(v);", "const float r = std::round(v);"),
+    # quantizer: Q4_0 scale from the magnitude, sign dropped
+    "quant_q4_unsigned": ("m = std::fabs(w[e]) > std::fabs(m) ? w[e] : m;", "m = std::fabs(w[e]) > std::fabs(m) ? std::fabs(w[e]) : m;"),
+    # quantizer: Q4_0 takes the last element of largest magnitude
+    "quant_q4_last_tie": ("m = std::fabs(w[e]) > std::fabs(m) ? w[e] : m;", "m = std::fabs(w[e]) >= std::fabs(m) ? w[e] : m;"),
+    # quantizer: Q8_0 divides by 128
+    "quant_q8_divisor": ("d16 = double_to_half(double(a / 127.0f));", "d16 = double_to_half(double(a / 128.0f));"),
+    # quantizer: int8 block-64 maximum over the first half of the block only
+    "quant_i8_half_block": ("for (int e = 0; e < E; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;\n                const float s",
+                            "for (int e = 0; e < 32; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;\n                const float s"),
+    # quantizer: bf16 widened with the wrong shift
+    "quant_bf16_shift": ("uint32_t bits = uint32_t(h) << 16;", "uint32_t bits = uint32_t(h) << 15;"),
 }
 
 
@@ -42,7 +56,7 @@ def test_pins_catch_mutant(name, tmp_path):
     assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
     mutant = lqref.build_variant(src.replace(old, new), str(tmp_path))
     failed = []
-    for pin in ALL_PINS:
+    for pin in ALL_PINS + QUANT_PINS:
         try:
             pin(mutant)
         except (AssertionError, ValueError):
