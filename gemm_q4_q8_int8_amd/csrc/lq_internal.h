@@ -78,9 +78,20 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #ifndef LQ_GEMV_UNR_I8
 #define LQ_GEMV_UNR_I8 2
 #endif
-#ifndef LQ_GEMV_MIN_UNITS
-#define LQ_GEMV_MIN_UNITS 2
+// Fewest units a wave keeps when K is split, per format (a unit is 1, 2 or
+// 4 KB of codes per wave for Q4_0, Q8_0, int8 block-64).
+#ifndef LQ_GEMV_MIN_UNITS_Q4
+#define LQ_GEMV_MIN_UNITS_Q4 8
 #endif
+#ifndef LQ_GEMV_MIN_UNITS_Q8
+#define LQ_GEMV_MIN_UNITS_Q8 8
+#endif
+#ifndef LQ_GEMV_MIN_UNITS_I8
+#define LQ_GEMV_MIN_UNITS_I8 2
+#endif
+inline int gemv_min_units(int fmt) {
+    return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kQ8_0 ? LQ_GEMV_MIN_UNITS_Q8 : LQ_GEMV_MIN_UNITS_I8);
+}
 
 struct GemvDesc {
     const uint8_t* codes;   // code plane (tiled)
