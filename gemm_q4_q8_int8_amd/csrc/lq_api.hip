@@ -138,6 +138,16 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
         nu[i] = g[i]->K / lq::unit_elems(fmt);
     }
     split_k(fmt, cus, tiles, nu, std::vector<int64_t>(n, 1), S);
+    // When every matrix splits K at least LQ_GEMV_WIDE_FROM ways, the launch
+    // uses 16-wave workgroups: four of the K slices move inside a workgroup
+    // (summed in LDS), leaving fewer or no split-K round trips.
+    int waves = 4;
+    bool wide = true;
+    for (int i = 0; i < n; ++i) wide = wide && S[i] >= LQ_GEMV_WIDE_FROM;
+    if (wide) {
+        waves = 16;
+        for (int i = 0; i < n; ++i) S[i] = (S[i] + 3) / 4;
+    }
     float* part = nullptr;
     uint32_t* cntp = nullptr;
     bool any_split = false;
@@ -174,7 +184,7 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
     }
     a.count = n;
     a.total_wgs = int32_t(wgs);
-    const hipError_t e = lq::launch_gemv(fmt, xdt, a, stream);
+    const hipError_t e = lq::launch_gemv(fmt, xdt, waves, a, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMV launch");
     return LQ_OK;
 }

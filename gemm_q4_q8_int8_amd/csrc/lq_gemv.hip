@@ -12,8 +12,9 @@
 //   * The activations are the same for every lane, so they are read with
 //     scalar loads (s_load into SGPRs, served by the scalar cache) and feed
 //     the vector FMAs as scalar operands: no LDS staging, no barrier, no VGPRs.
-//   * A workgroup of 4 waves takes one tile and splits its units four ways;
-//     the four partial sums meet in LDS in a fixed order.  When the matrices
+//   * A workgroup of 4 waves (16 for launches of small matrices) takes one
+//     tile and splits its units among its waves; the partial sums meet in
+//     LDS in a fixed order.  When the matrices
 //     of a launch have too few tiles to fill the chip (one 2048-row matrix is
 //     32 tiles), K is also split across S workgroups per tile: each writes
 //     its slice's sums to a per-device scratch area and bumps the tile's
@@ -234,13 +235,16 @@ __device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S)
     return t;
 }
 
-template <int FMT, int XDT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
+// W waves per workgroup split a tile's K slice W ways (4, or 16 for
+// launches whose matrices would otherwise split K across 4+ workgroups: the
+// split then stays inside the workgroup and needs no split-K round trips).
+template <int FMT, int XDT, int W>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     constexpr int P = unit_parts(FMT);
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
     constexpr int UNR = unroll_of<FMT>();
-    __shared__ float red[4][kTileRows];
+    __shared__ float red[W][kTileRows];
 
     // Matrix of this workgroup: the last descriptor whose first workgroup is
     // not after ours (uniform, scalar compares).
@@ -260,8 +264,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
     // Units [ua, ub) of this wave: slice `slice` of S, then quarter w of it.
     const int sa = int(int64_t(nu) * slice / S);
     const int sb = int(int64_t(nu) * (slice + 1) / S);
-    const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / 4);
-    const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / 4);
+    const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / W);
+    const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / W);
 
     // Uniform tile bases plus 32-bit per-lane offsets (scalar base + vector
     // offset addressing).
@@ -298,7 +302,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
     red[w][r] = acc;
     __syncthreads();
     if (w != 0) return;
-    const float v = (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < W; i += 4) v += (red[i][r] + red[i + 1][r]) + (red[i + 2][r] + red[i + 3][r]);
     const size_t row = size_t(tile) * kTileRows + size_t(r);
     if (S == 1) {
         if (r < nr) D.y[row] = v;
@@ -327,10 +333,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
 }
 
 template <int FMT>
-hipError_t launch_fmt(int xdt, const GemvArgs& a, hipStream_t stream) {
-    const dim3 grid(unsigned(a.total_wgs)), block(kGemvThreads);
-    if (xdt == kF32) hipLaunchKernelGGL((gemv_kernel<FMT, kF32>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemv_kernel<FMT, kF16>), grid, block, 0, stream, a);
+hipError_t launch_fmt(int xdt, int waves, const GemvArgs& a, hipStream_t stream) {
+    const dim3 grid(unsigned(a.total_wgs)), block(unsigned(64 * waves));
+    if (waves == 16) {
+        if (xdt == kF32) hipLaunchKernelGGL((gemv_kernel<FMT, kF32, 16>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((gemv_kernel<FMT, kF16, 16>), grid, block, 0, stream, a);
+    } else {
+        if (xdt == kF32) hipLaunchKernelGGL((gemv_kernel<FMT, kF32, 4>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((gemv_kernel<FMT, kF16, 4>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -361,11 +372,12 @@ hipError_t gemv_scratch(float** part, uint32_t** cnt) {
     return hipSuccess;
 }
 
-hipError_t launch_gemv(int fmt, int xdt, const GemvArgs& a, hipStream_t stream) {
+hipError_t launch_gemv(int fmt, int xdt, int waves, const GemvArgs& a, hipStream_t stream) {
+    if (waves != 4 && waves != 16) return hipErrorInvalidValue;
     switch (fmt) {
-        case kQ4_0: return launch_fmt<kQ4_0>(xdt, a, stream);
-        case kQ8_0: return launch_fmt<kQ8_0>(xdt, a, stream);
-        case kI8B64: return launch_fmt<kI8B64>(xdt, a, stream);
+        case kQ4_0: return launch_fmt<kQ4_0>(xdt, waves, a, stream);
+        case kQ8_0: return launch_fmt<kQ8_0>(xdt, waves, a, stream);
+        case kI8B64: return launch_fmt<kI8B64>(xdt, waves, a, stream);
         default: return hipErrorInvalidValue;
     }
 }

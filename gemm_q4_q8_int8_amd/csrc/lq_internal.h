@@ -59,6 +59,12 @@ __host__ __device__ inline TiledPos tiled_pos(int fmt, int64_t N, int64_t nu, in
 // ---------------------------------------------------------------- GEMV ----
 constexpr int kMaxBatch = 16;       // descriptors per grouped launch
 constexpr int kGemvThreads = 256;   // 4 waves: one tile, K split four ways
+// Waves per workgroup of a GEMV launch whose matrices all split K across at
+// least this many workgroups of 4 waves: the split then moves inside one
+// workgroup of 16 waves.
+#ifndef LQ_GEMV_WIDE_FROM
+#define LQ_GEMV_WIDE_FROM 4
+#endif
 // Split-K scratch held by the library on every device (static device arrays):
 // partial sums of the K slices of a tile, and one arrival counter per tile.
 constexpr int64_t kGemvPartFloats = int64_t(1) << 20;   // 4 MiB
@@ -114,7 +120,7 @@ struct GemvArgs {
     int32_t total_wgs;
 };
 
-hipError_t launch_gemv(int fmt, int xdt, const GemvArgs& args, hipStream_t stream);
+hipError_t launch_gemv(int fmt, int xdt, int waves, const GemvArgs& args, hipStream_t stream);
 // Device addresses of this device's split-K scratch (looked up once per device).
 hipError_t gemv_scratch(float** part, uint32_t** cnt);
 
