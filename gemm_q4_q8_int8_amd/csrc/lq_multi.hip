@@ -27,9 +27,12 @@
 //   * The MFMA output lane (r, j) then holds tokens 4j..4j+3 of weight rows
 //     4r + m, so the scales it needs are the four consecutive ones of rows
 //     4r..4r+3: one 8- or 16-byte load per unit.
-//   * The k order inside a block is free as long as A and B agree: lane
-//     group j takes elements 4j..4j+3 and 16+4j..16+4j+3, which for Q4_0 are
-//     exactly the low and high nibbles of code dword j.
+//   * The k order inside a block is free as long as A and B agree.  Q4_0:
+//     lane group j takes elements 4j..4j+3 and 16+4j..16+4j+3, exactly the
+//     low and high nibbles of code dword j.  int8: lane group j takes
+//     elements 8j..8j+7 (the two 16-byte parts of a 32-element step are
+//     transposed as double dwords), so its activations are one 16-byte
+//     load.
 #include "lq_frag.h"
 
 namespace lq {
@@ -122,8 +125,14 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
             const _Float16* xp = L.xrow + size_t(uu) * E;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                b[k].xl[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks);
-                b[k].xh[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks + 16);
+                if constexpr (FMT == kQ4_0) {
+                    b[k].xl[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks);
+                    b[k].xh[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks + 16);
+                } else {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(xp + 32 * ks);
+                    b[k].xl[ks] = u32x2{v.x, v.y};
+                    b[k].xh[ks] = u32x2{v.z, v.w};
+                }
             }
         }
         // Every load of the batch is issued before any of its data is used.
@@ -131,9 +140,20 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
             if (u + k >= L.ub) continue;
+            // Q4_0: t[0] slot m = code dword j of row 4r + m.  int8: t[2 ks]
+            // and t[2 ks + 1] slot m = codes 8j .. 8j+3 and 8j+4 .. 8j+7 of
+            // step ks of row 4r + m (a transpose of double dwords).
             u32x4 t[P];
+            if constexpr (FMT == kQ4_0) {
+                t[0] = xpose(b[k].c[0]);
+            } else {
 #pragma unroll
-            for (int p = 0; p < P; ++p) t[p] = xpose(b[k].c[p]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 p0 = b[k].c[2 * ks], p1 = b[k].c[2 * ks + 1];
+                    t[2 * ks] = xpose(u32x4{p0.x, p0.z, p1.x, p1.z});
+                    t[2 * ks + 1] = xpose(u32x4{p0.y, p0.w, p1.y, p1.w});
+                }
+            }
             half8_t xa[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) xa[ks] = x_frag<FMT>(b[k].xl[ks], b[k].xh[ks]);
@@ -210,7 +230,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     L.s_unit = uint32_t(nr) * SB;
 #pragma unroll
     for (int m = 0; m < 4; ++m) L.s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
-    L.xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + 4 * g;
+    // Q4_0 lane group g takes elements 4g..4g+3 and 16+4g.. of a block (the
+    // nibbles of code dword g); int8 lane group g takes elements 8g..8g+7.
+    L.xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + (FMT == kQ4_0 ? 4 : 8) * g;
     L.ua = ua;
     L.ub = ub;
 
