@@ -97,3 +97,43 @@ def test_quantize_then_gemv(oracle):
         q, s = oracle.quantize(ORACLE_FMT[fmt], w, N, K)
         yr, S = oracle.gemv(ORACLE_FMT[fmt], q, s, x, N, K)
         assert gu.ratio(y, yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, fmt
+
+
+@pytest.fixture(scope="module")
+def x_max_k():
+    return lqgen.activations(4096, 1 << 25, np.float32)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+def test_max_k_full_tile(oracle, fmt, x_max_k):
+    """K at the documented maximum (2^25) with a full 64-row tile: the 32-bit
+    offsets inside a tile reach their largest values.  Weights are generated
+    and quantized on the GPU; the oracle quantizes the same fp16 rows on the
+    host (the quantizers agree bit for bit) and checks sampled rows of the
+    GEMV (K split across many workgroups) and of a two-token multi-token
+    GEMV."""
+    N, K = 64, 1 << 25
+    say("max K", fmt, N, K)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    W16 = torch.randn(N, K, dtype=torch.float16, device="cuda", generator=g) * 0.05
+    Wd = empty_packed(gu.FMT[fmt], N, K)
+    lq.lq_quantize(gu.FMT[fmt], W16, Wd, N, K)
+    x = x_max_k
+    y = gu.gemv(fmt, Wd, x, N, K)
+    # two tokens through the multi-token GEMV on the same weights
+    x16 = x.astype(np.float16)
+    X2 = np.stack([x16, -x16[::-1]])
+    Y2 = gu.gemv_multi(fmt, Wd, X2, 2, N, K)
+    for row in (0, 37, 63):
+        w_row = W16[row].cpu().numpy()
+        q, s = oracle.quantize(ORACLE_FMT[fmt], w_row, 1, K)
+        yr, S = oracle.gemv(ORACLE_FMT[fmt], q, s, x, 1, K)
+        r = gu.ratio(y[row:row + 1], yr, S, gu.GEMV_REL, gu.GEMV_ABS)
+        assert r <= 1.0, (fmt, row, r)
+        Yr, S2 = oracle.gemm(ORACLE_FMT[fmt], q, s, X2, 2, 1, K)
+        r2 = gu.ratio(Y2[:, row:row + 1], Yr, S2, gu.GEMV_REL, gu.GEMV_ABS)
+        assert r2 <= 1.0, (fmt, row, "multi", r2)
+    del W16, Wd
+    torch.cuda.empty_cache()
