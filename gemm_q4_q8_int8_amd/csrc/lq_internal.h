@@ -136,6 +136,12 @@ constexpr int kMultiMaxTokens = 16;   // tokens of one MFMA fragment
 #ifndef LQ_MULTI_UNR_I8
 #define LQ_MULTI_UNR_I8 2
 #endif
+// Q4_0 launches whose waves all have more than LQ_MULTI_UNR_Q4 and at most
+// this many units (K = 896 on one slice: 7) load them in one batch instead of
+// two.  Longer loops keep the smaller batch, which needs fewer registers.
+#ifndef LQ_MULTI_UNR_Q4_ONE
+#define LQ_MULTI_UNR_Q4_ONE 7
+#endif
 
 struct MultiDesc {
     const uint8_t* codes;   // code plane (tiled)

@@ -45,11 +45,6 @@ template <int FMT>
 constexpr int steps_of() { return FMT == kI8B64 ? 2 : 1; }
 
 template <int FMT>
-constexpr int multi_unroll() {
-    return FMT == kQ4_0 ? LQ_MULTI_UNR_Q4 : (FMT == kQ8_0 ? LQ_MULTI_UNR_Q8 : LQ_MULTI_UNR_I8);
-}
-
-template <int FMT>
 struct MUnit {
     static constexpr int P = unit_parts(FMT);
     static constexpr int KS = steps_of<FMT>();
@@ -87,13 +82,12 @@ struct WaveLoop {
 // acc[m][i] += sum over the wave's units of w[4r+m, k] X[4j+i, k].  FULL: the
 // tile has 64 rows, so the four scales of rows 4r..4r+3 are one load.  The
 // choice is made once per workgroup so the load phase has no branches.
-template <int FMT, bool FULL>
+template <int FMT, int UNR, bool FULL>
 __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
     constexpr int P = unit_parts(FMT);
     constexpr int SB = scale_bytes(FMT);
     constexpr int E = unit_elems(FMT);
     constexpr int KS = steps_of<FMT>();
-    constexpr int UNR = multi_unroll<FMT>();
     for (int u = L.ua; u < L.ub; u += UNR) {
         MUnit<FMT> b[UNR];
 #pragma unroll
@@ -190,7 +184,8 @@ __device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S)
     return t;
 }
 
-template <int FMT>
+// UNR: units whose loads one wave issues before computing them.
+template <int FMT, int UNR>
 __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArgs a) {
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
@@ -237,8 +232,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     L.ub = ub;
 
     f32x4 acc[4] = {};
-    if (full) accumulate<FMT, true>(L, acc);
-    else accumulate<FMT, false>(L, acc);
+    if (full) accumulate<FMT, UNR, true>(L, acc);
+    else accumulate<FMT, UNR, false>(L, acc);
 
     // Sum the four waves' K quarters; wave w then owns token 4g + w of rows
     // 4r .. 4r+3.
@@ -298,12 +293,32 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
 
 }  // namespace
 
+// Fewest and most units that the waves of a launch loop over: per matrix,
+// ceil(ceil(nu / S) / 4) (the waves of one slice differ by at most one).
+static void wave_units(const MultiArgs& a, int& least, int& most) {
+    least = INT32_MAX;
+    most = 0;
+    for (int i = 0; i < a.count; ++i) {
+        const int slice = (a.d[i].nu + a.d[i].S - 1) / a.d[i].S;
+        least = min(least, (slice + 3) / 4);
+        most = max(most, (slice + 3) / 4);
+    }
+}
+
 hipError_t launch_gemv_multi(int fmt, const MultiArgs& a, hipStream_t stream) {
     const dim3 grid(unsigned(a.total_wgs)), block(kGemvThreads);
     switch (fmt) {
-        case kQ4_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ4_0>, grid, block, 0, stream, a); break;
-        case kQ8_0: hipLaunchKernelGGL(gemv_multi_kernel<kQ8_0>, grid, block, 0, stream, a); break;
-        case kI8B64: hipLaunchKernelGGL(gemv_multi_kernel<kI8B64>, grid, block, 0, stream, a); break;
+        case kQ4_0: {
+            int least, most;
+            wave_units(a, least, most);
+            if (least > LQ_MULTI_UNR_Q4 && most <= LQ_MULTI_UNR_Q4_ONE)
+                hipLaunchKernelGGL((gemv_multi_kernel<kQ4_0, LQ_MULTI_UNR_Q4_ONE>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((gemv_multi_kernel<kQ4_0, LQ_MULTI_UNR_Q4>), grid, block, 0, stream, a);
+            break;
+        }
+        case kQ8_0: hipLaunchKernelGGL((gemv_multi_kernel<kQ8_0, LQ_MULTI_UNR_Q8>), grid, block, 0, stream, a); break;
+        case kI8B64: hipLaunchKernelGGL((gemv_multi_kernel<kI8B64, LQ_MULTI_UNR_I8>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -36,10 +36,12 @@ def device():
 
 # (fmt, M, N, K): tails in rows (N % 64) and tokens, single-block rows, long
 # K (split across workgroups when N is small), and big-N single-slice cases.
+# Q4_0 waves with 5 to 7 units load them as one batch of 7: K = 896 fills it,
+# K = 704 (22 units: waves of 5 and 6) and 640 leave slots of it unused.
 MULTI_SHAPES = [
     ("q4_0", 1, 1, 32), ("q4_0", 2, 5, 64), ("q4_0", 3, 67, 96), ("q4_0", 16, 64, 896),
     ("q4_0", 5, 130, 960), ("q4_0", 8, 300, 2048), ("q4_0", 13, 33, 11008), ("q4_0", 16, 2500, 896),
-    ("q4_0", 4, 17, 25600),
+    ("q4_0", 4, 17, 25600), ("q4_0", 3, 129, 704), ("q4_0", 9, 3000, 640),
     ("q8_0", 1, 3, 32), ("q8_0", 2, 70, 512), ("q8_0", 7, 130, 2048), ("q8_0", 16, 64, 8192),
     ("q8_0", 11, 200, 5632), ("q8_0", 16, 1100, 1024),
     ("i8b64", 1, 1, 64), ("i8b64", 3, 77, 128), ("i8b64", 16, 256, 2048), ("i8b64", 6, 45, 5632),
