@@ -97,11 +97,11 @@ lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
 // share each 64-row tile of matrix i.  When the launch has fewer tiles than
 // about LQ_GEMV_WGS_PER_CU workgroups per CU, every matrix is split so that
 // its workgroups get about the same number of units (the launch's total work
-// spread over that many workgroups), never below the format's minimum units
-// per wave (gemv_min_units).  Equal work per workgroup keeps a long-K matrix from becoming the
-// tail of the launch.  M[i] tokens of partials per row count against the
+// spread over that many workgroups), never below min_units per wave (per
+// format: gemv_min_units, multi_min_units).  Equal work per workgroup keeps
+// a long-K matrix from becoming the tail of the launch.  M[i] tokens of partials per row count against the
 // split-K scratch; if it does not fit, nothing is split.
-void split_k(int fmt, int cus, const std::vector<int64_t>& tiles, const std::vector<int64_t>& nu,
+void split_k(int min_units, int cus, const std::vector<int64_t>& tiles, const std::vector<int64_t>& nu,
              const std::vector<int64_t>& M, std::vector<int64_t>& S) {
     const size_t n = tiles.size();
     int64_t total_tiles = 0, work = 0;
@@ -115,7 +115,7 @@ void split_k(int fmt, int cus, const std::vector<int64_t>& tiles, const std::vec
     const double per_wg = double(work) / double(target);   // units per workgroup
     int64_t part = 0, cnt = 0;
     for (size_t i = 0; i < n; ++i) {
-        const int64_t cap = std::max<int64_t>(1, nu[i] / (4 * lq::gemv_min_units(fmt)));
+        const int64_t cap = std::max<int64_t>(1, nu[i] / (4 * min_units));
         const int64_t want = std::max<int64_t>(1, int64_t(double(nu[i]) / per_wg + 0.5));
         S[i] = std::min(want, cap);
         if (S[i] > 1) {
@@ -137,7 +137,7 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
         tiles[i] = (g[i]->N + lq::kTileRows - 1) / lq::kTileRows;
         nu[i] = g[i]->K / lq::unit_elems(fmt);
     }
-    split_k(fmt, cus, tiles, nu, std::vector<int64_t>(n, 1), S);
+    split_k(lq::gemv_min_units(fmt), cus, tiles, nu, std::vector<int64_t>(n, 1), S);
     // When every matrix splits K at least LQ_GEMV_WIDE_FROM ways, the launch
     // uses 16-wave workgroups: four of the K slices move inside a workgroup
     // (summed in LDS), leaving fewer or no split-K round trips.
@@ -219,7 +219,7 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
     }
     std::vector<int64_t> Ms(n);
     for (int i = 0; i < n; ++i) Ms[i] = g[i]->M;
-    split_k(fmt, cus, tiles, nu, Ms, S);
+    split_k(lq::multi_min_units(fmt), cus, tiles, nu, Ms, S);
     float* part = nullptr;
     uint32_t* cntp = nullptr;
     bool any_split = false;

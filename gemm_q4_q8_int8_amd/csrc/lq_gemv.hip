@@ -20,9 +20,14 @@
 //     its slice's sums to a per-device scratch area and bumps the tile's
 //     arrival counter; the last one to arrive adds the S slices in slice
 //     order (deterministic) and writes y.
-//   * Each wave issues the loads of UNR units before it computes any of them
-//     (all in flight at once); with 8 waves per SIMD resident that keeps
-//     enough bytes in flight to cover HBM latency.
+//   * Each wave issues the loads of a batch of UNR units before it computes
+//     any of them (all in flight at once, consumed in load order).  UNR is
+//     chosen per launch so that the batches split a wave's units evenly: a
+//     slot past the wave's last unit still loads and computes (its sum is
+//     masked off), since per-slot branches let the compiler sink loads below
+//     the first slot's arithmetic.  Q4_0 (most arithmetic per byte) takes
+//     up to 8 units per batch, Q8_0 2 and int8 block-64 1: with the waves
+//     resident per SIMD, larger batches were measured slower.
 //   * Q4_0 nibbles become exact fp16 values (q - 8) with one v_and_or_b32
 //     (nibble into an fp16 mantissa under exponent 2^10) and one v_pk_add_f16
 //     per two weights.  fp32 activations: v_fma_mix_f32 multiplies that fp16
@@ -189,9 +194,12 @@ struct Unit {
     uint32_t s;   // raw scale bits (fp16 in the low half, or fp32)
 };
 
-// scale * sum over unit u of code * x.
+// scale * sum over unit u of code * x, added to acc.  keep is all ones, or
+// zero for a slot past the wave's last unit (its sum is dropped bit-wise, so
+// even an infinite or NaN sum adds nothing).
 template <int FMT, int XDT>
-__device__ __forceinline__ float unit_fma(const Unit<FMT>& b, const void* xv, int u, float acc) {
+__device__ __forceinline__ float unit_fma(const Unit<FMT>& b, const void* xv, int u, uint32_t keep,
+                                          float acc) {
     constexpr int E = unit_elems(FMT);
     float dot;
     if constexpr (XDT == kF32) {
@@ -208,13 +216,12 @@ __device__ __forceinline__ float unit_fma(const Unit<FMT>& b, const void* xv, in
     float d;
     if constexpr (FMT == kI8B64) d = __uint_as_float(b.s);
     else d = (float)__builtin_bit_cast(_Float16, uint16_t(b.s));
-    return __builtin_fmaf(d, dot, acc);
+    return __builtin_fmaf(d, __uint_as_float(__float_as_uint(dot) & keep), acc);
 }
 
-// Units whose loads one wave issues before computing (register budget: the
-// codes of UNR units stay live).
-template <int FMT>
-constexpr int unroll_of() { return FMT == kQ4_0 ? LQ_GEMV_UNR_Q4 : (FMT == kQ8_0 ? LQ_GEMV_UNR_Q8 : LQ_GEMV_UNR_I8); }
+// Largest batch of units one wave loads before computing them (register
+// budget: the codes of a batch stay live).
+constexpr int unroll_cap(int fmt) { return fmt == kQ4_0 ? LQ_GEMV_UNR_Q4 : (fmt == kQ8_0 ? LQ_GEMV_UNR_Q8 : LQ_GEMV_UNR_I8); }
 
 // sum_{j < S} p[j * pitch] in slice order, loads issued eight at a time so
 // their latencies overlap.
@@ -238,12 +245,12 @@ __device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S)
 // W waves per workgroup split a tile's K slice W ways (4, or 16 for
 // launches whose matrices would otherwise split K across 4+ workgroups: the
 // split then stays inside the workgroup and needs no split-K round trips).
-template <int FMT, int XDT, int W>
+// Each wave loads UNR units, then computes them, until its units are done.
+template <int FMT, int XDT, int W, int UNR>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     constexpr int P = unit_parts(FMT);
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
-    constexpr int UNR = unroll_of<FMT>();
     __shared__ float red[W][kTileRows];
 
     // Matrix of this workgroup: the last descriptor whose first workgroup is
@@ -294,9 +301,13 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
             if constexpr (SB == 2) b[k].s = *reinterpret_cast<const uint16_t*>(sbase + so);
             else b[k].s = *reinterpret_cast<const uint32_t*>(sbase + so);
         }
+        // Every load of the batch is issued before any of its data is used,
+        // and every slot is computed: a branch per slot let the compiler sink
+        // loads below the first slot's arithmetic.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < UNR; ++k)
-            if (u + k < ub) acc = unit_fma<FMT, XDT>(b[k], x, u + k, acc);
+            acc = unit_fma<FMT, XDT>(b[k], x, min(u + k, ub - 1), u + k < ub ? ~0u : 0u, acc);
     }
 
     red[w][r] = acc;
@@ -332,17 +343,39 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     if (r == 0) __hip_atomic_store(&D.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int FMT, int XDT, int W, int UNR>
+hipError_t launch_unr(int unr, const GemvArgs& a, hipStream_t stream) {
+    if constexpr (UNR > 1) {
+        if (unr < UNR) return launch_unr<FMT, XDT, W, UNR - 1>(unr, a, stream);
+    }
+    hipLaunchKernelGGL((gemv_kernel<FMT, XDT, W, UNR>), dim3(unsigned(a.total_wgs)), dim3(64u * W), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+// Batch size of a launch: its waves have at most u units (ceil(ceil(nu / S)
+// / W)); they run in ceil(u / cap) batches of ceil(u / batches) units, so
+// that no batch loads and computes many slots past a wave's last unit.
+int launch_unroll(int fmt, int waves, const GemvArgs& a) {
+    int u = 1;
+    for (int i = 0; i < a.count; ++i) {
+        const int slice = (a.d[i].nu + a.d[i].S - 1) / a.d[i].S;
+        u = max(u, (slice + waves - 1) / waves);
+    }
+    const int batches = (u + unroll_cap(fmt) - 1) / unroll_cap(fmt);
+    return (u + batches - 1) / batches;
+}
+
 template <int FMT>
 hipError_t launch_fmt(int xdt, int waves, const GemvArgs& a, hipStream_t stream) {
-    const dim3 grid(unsigned(a.total_wgs)), block(unsigned(64 * waves));
+    constexpr int CAP = unroll_cap(FMT);
+    const int unr = launch_unroll(FMT, waves, a);
     if (waves == 16) {
-        if (xdt == kF32) hipLaunchKernelGGL((gemv_kernel<FMT, kF32, 16>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((gemv_kernel<FMT, kF16, 16>), grid, block, 0, stream, a);
-    } else {
-        if (xdt == kF32) hipLaunchKernelGGL((gemv_kernel<FMT, kF32, 4>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((gemv_kernel<FMT, kF16, 4>), grid, block, 0, stream, a);
+        if (xdt == kF32) return launch_unr<FMT, kF32, 16, CAP>(unr, a, stream);
+        return launch_unr<FMT, kF16, 16, CAP>(unr, a, stream);
     }
-    return hipGetLastError();
+    if (xdt == kF32) return launch_unr<FMT, kF32, 4, CAP>(unr, a, stream);
+    return launch_unr<FMT, kF16, 4, CAP>(unr, a, stream);
 }
 
 std::mutex g_scratch_mu;

@@ -74,15 +74,18 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #ifndef LQ_GEMV_WGS_PER_CU
 #define LQ_GEMV_WGS_PER_CU 8
 #endif
-// Units whose loads one wave issues before computing them (per format).
+// Most units whose loads one wave issues before computing them (per
+// format).  A launch whose waves have at most u units runs them in
+// ceil(u / cap) batches of equal size (the kernel is instantiated for every
+// batch size up to the cap).
 #ifndef LQ_GEMV_UNR_Q4
 #define LQ_GEMV_UNR_Q4 8
 #endif
 #ifndef LQ_GEMV_UNR_Q8
-#define LQ_GEMV_UNR_Q8 4
+#define LQ_GEMV_UNR_Q8 2
 #endif
 #ifndef LQ_GEMV_UNR_I8
-#define LQ_GEMV_UNR_I8 2
+#define LQ_GEMV_UNR_I8 1
 #endif
 // Fewest units a wave keeps when K is split, per format (a unit is 1, 2 or
 // 4 KB of codes per wave for Q4_0, Q8_0, int8 block-64).
@@ -90,7 +93,7 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #define LQ_GEMV_MIN_UNITS_Q4 8
 #endif
 #ifndef LQ_GEMV_MIN_UNITS_Q8
-#define LQ_GEMV_MIN_UNITS_Q8 8
+#define LQ_GEMV_MIN_UNITS_Q8 4
 #endif
 #ifndef LQ_GEMV_MIN_UNITS_I8
 #define LQ_GEMV_MIN_UNITS_I8 2
@@ -98,6 +101,9 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 inline int gemv_min_units(int fmt) {
     return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kQ8_0 ? LQ_GEMV_MIN_UNITS_Q8 : LQ_GEMV_MIN_UNITS_I8);
 }
+// The same for the multi-token GEMV, whose split K also moves M tokens of
+// partial sums per row through the scratch area.
+inline int multi_min_units(int fmt) { return fmt == kI8B64 ? 2 : 8; }
 
 struct GemvDesc {
     const uint8_t* codes;   // code plane (tiled)
