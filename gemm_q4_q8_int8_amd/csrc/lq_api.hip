@@ -4,9 +4,9 @@
 #include "../../include/lq.h"
 #include "lq_internal.h"
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
-#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -127,6 +127,18 @@ void split_k(int min_units, int cus, const std::vector<int64_t>& tiles, const st
         for (size_t i = 0; i < n; ++i) S[i] = 1;
 }
 
+// Launch order of a grouped launch's matrices: most K slices per tile first
+// (stable).  Workgroups are dispatched, and their loads served by HBM, about
+// in launch order, so the split-K round trip of the split matrices (partials,
+// arrival counter, ordered sum) overlaps the stream of the others instead of
+// trailing the launch.
+std::vector<int> split_first(const std::vector<int64_t>& S) {
+    std::vector<int> ord(S.size());
+    for (size_t i = 0; i < ord.size(); ++i) ord[i] = int(i);
+    std::stable_sort(ord.begin(), ord.end(), [&](int p, int q) { return S[p] > S[q]; });
+    return ord;
+}
+
 // One grouped GEMV launch: up to kMaxBatch descriptors of one format and
 // activation dtype, K split by split_k.
 lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>& g, int cus,
@@ -156,11 +168,13 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
         const hipError_t e = lq::gemv_scratch(&part, &cntp);
         if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
     }
+    const std::vector<int> ord = split_first(S);
     lq::GemvArgs a = {};
     int64_t wgs = 0, part_off = 0, cnt_off = 0;
-    for (int i = 0; i < n; ++i) {
+    for (int j = 0; j < n; ++j) {
+        const int i = ord[j];
         const lq_gemv_desc& d = *g[i];
-        lq::GemvDesc& o = a.d[i];
+        lq::GemvDesc& o = a.d[j];
         o.codes = static_cast<const uint8_t*>(d.W);
         o.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(fmt, d.N, d.K));
         o.x = d.x;
@@ -228,11 +242,13 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
         const hipError_t e = lq::gemv_scratch(&part, &cntp);
         if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
     }
+    const std::vector<int> ord = split_first(S);
     lq::MultiArgs a = {};
     int64_t wgs = 0, part_off = 0, cnt_off = 0;
-    for (int i = 0; i < n; ++i) {
+    for (int j = 0; j < n; ++j) {
+        const int i = ord[j];
         const lq_gemv_multi_desc& d = *g[i];
-        lq::MultiDesc& o = a.d[i];
+        lq::MultiDesc& o = a.d[j];
         o.codes = static_cast<const uint8_t*>(d.W);
         o.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(fmt, d.N, d.K));
         o.x = static_cast<const _Float16*>(d.X);
