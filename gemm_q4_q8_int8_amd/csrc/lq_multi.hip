@@ -100,7 +100,7 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
                     reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
             const uint8_t* sp = L.sbase + uu * L.s_unit;
             if constexpr (FULL && SB == 2) {
-                const u32x2 v = *reinterpret_cast<const u32x2*>(sp + L.s_row[0]);
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sp + L.s_row[0]));
                 b[k].s[0] = v.x;
                 b[k].s[1] = v.y;
             } else if constexpr (FULL) {
@@ -112,7 +112,8 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
             } else {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    if constexpr (SB == 2) b[k].s[m] = *reinterpret_cast<const uint16_t*>(sp + L.s_row[m]);
+                    if constexpr (SB == 2)
+                        b[k].s[m] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp + L.s_row[m]));
                     else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + L.s_row[m]);
                 }
             }
