@@ -24,7 +24,7 @@ EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq
            "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_quantize", "lq_dequant_f32",
            "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi", "lq_gemv_multi_batch",
            "lq_gemm_workspace_bytes",
-           "lq_gemm",
+           "lq_gemm", "lq_gemm_batch",
            "lq_matmul", "lq_status_str", "lq_last_error")
 
 
@@ -51,6 +51,12 @@ class lq_gemv_multi_desc(ctypes.Structure):
                 ("X", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("M", ctypes.c_int64),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
+
+class lq_gemm_desc(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
+LQ_GEMM_MAX_GROUP = 4
 
 _lib = None
 
@@ -82,6 +88,7 @@ def load(path: str = LIB_PATH):
         "lq_gemv_multi_batch": ([ctypes.POINTER(lq_gemv_multi_desc), i32, vp], i32),
         "lq_gemm_workspace_bytes": ([i32, i64, i64, i64], sz),
         "lq_gemm": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
+        "lq_gemm_batch": ([i32, vp, i32, i64, i64, ctypes.POINTER(lq_gemm_desc), i32, vp, sz, vp], i32),
         "lq_matmul": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_status_str": ([i32], ctypes.c_char_p),
         "lq_last_error": ([], ctypes.c_char_p),
@@ -227,6 +234,16 @@ def lq_gemm(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=0, stream=None, xdt=None):
     xdt = _xdt(X) if xdt is None else xdt
     _check(load().lq_gemm(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K, _ptr(ws), ws_bytes,
                           _stream(stream)))
+
+
+def lq_gemm_batch(fmt, X, M, K, descs, ws=None, ws_bytes=0, stream=None, xdt=None):
+    """descs: sequence of (W, Y, N): weight matrices sharing X, M and K."""
+    xdt = _xdt(X) if xdt is None else xdt
+    arr = (lq_gemm_desc * max(1, len(descs)))()
+    for i, (W, Y, N) in enumerate(descs):
+        arr[i] = lq_gemm_desc(_ptr(W), _ptr(Y), N)
+    _check(load().lq_gemm_batch(_fmt(fmt), _ptr(X), xdt, M, K, arr, len(descs), _ptr(ws), ws_bytes,
+                                _stream(stream)))
 
 
 def lq_matmul(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=0, stream=None, xdt=None):

@@ -282,6 +282,8 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
 
 extern "C" {
 
+static_assert(LQ_GEMM_MAX_GROUP == lq::kMaxGemmGroup, "GEMM group size");
+
 int32_t lq_abi_version(void) { return LQ_ABI_VERSION; }
 
 lq_status lq_init(void) {
@@ -453,24 +455,54 @@ size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
 
 lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
                   int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
-    LQ_TRY(check_fmt_shape(fmt, N, K));
+    lq_gemm_desc d;
+    d.W = W;
+    d.Y = Y;
+    d.N = N;
+    return lq_gemm_batch(fmt, X, xdt, M, K, &d, 1, ws, ws_bytes, stream);
+}
+
+lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int64_t K, const lq_gemm_desc* descs,
+                        int32_t count, void* ws, size_t ws_bytes, void* stream) {
+    if (!descs) return fail(LQ_ERR_ARG, "descs is NULL");
+    if (count < 1 || count > LQ_GEMM_MAX_GROUP)
+        return fail(LQ_ERR_ARG, "count=%d out of range [1, %d]", count, LQ_GEMM_MAX_GROUP);
     LQ_TRY(check_xdt(xdt));
     if (M < 1 || M > kMaxDim) return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, 2^31-1]", (long long)M);
     if (xdt != LQ_F16) return fail(LQ_ERR_UNSUPPORTED, "lq_gemm takes LQ_F16 activations");
     if (M * K > (int64_t(1) << 40)) return fail(LQ_ERR_SHAPE, "X too large");
-    LQ_TRY(check_ptr(W, 16, "W"));
     LQ_TRY(check_ptr(X, 16, "X"));
-    LQ_TRY(check_ptr(Y, 4, "Y"));
-    const size_t need = gemm_ws(fmt, M, N, K);
+    size_t need = 0;
+    for (int i = 0; i < count; ++i) {
+        LQ_TRY(check_fmt_shape(fmt, descs[i].N, K));
+        LQ_TRY(check_ptr(descs[i].W, 16, "W"));
+        LQ_TRY(check_ptr(descs[i].Y, 4, "Y"));
+        need = std::max(need, gemm_ws(fmt, M, descs[i].N, K));
+    }
+    if (use_lds_tile_gemm(fmt) && count > 1) need = 0;   // one launch, K not split
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, ws_bytes);
     if (ws && !aligned(ws, 16)) return fail(LQ_ERR_ALIGN, "ws is not 16-byte aligned");
     int cus = 0;
     LQ_TRY(device_cus(&cus));
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = use_lds_tile_gemm(fmt) ? lq::launch_gemm_q4_0(W, X, Y, M, N, K, ws, ws_bytes, cus, s)
-                                                : lq::launch_prefill(fmt, W, X, Y, M, N, K, ws, s);
-    return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
+    if (use_lds_tile_gemm(fmt)) {
+        const void* W[lq::kMaxGemmGroup];
+        float* Y[lq::kMaxGemmGroup];
+        int64_t N[lq::kMaxGemmGroup];
+        for (int i = 0; i < count; ++i) {
+            W[i] = descs[i].W;
+            Y[i] = descs[i].Y;
+            N[i] = descs[i].N;
+        }
+        const hipError_t e = lq::launch_gemm_q4_0(W, Y, N, count, X, M, K, ws, cus, s);
+        return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
+    }
+    for (int i = 0; i < count; ++i) {
+        const hipError_t e = lq::launch_prefill(fmt, descs[i].W, X, descs[i].Y, M, descs[i].N, K, ws, s);
+        if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+    }
+    return LQ_OK;
 }
 
 lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,

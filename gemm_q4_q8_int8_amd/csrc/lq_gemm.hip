@@ -47,37 +47,55 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256;
-constexpr int BN = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-// One ring slot: X (256 rows x 64 B), the codes of one block of the two
-// packed tiles (2 x 1 KB), their scales (2 x 256 B: a 2-byte load to LDS
-// fills one dword per lane, zero-extended), and 256 B that absorb the extra
-// loads of waves with nothing else to copy.
 constexpr int kXRowBytes = 64;
-constexpr int kWOff = BM * kXRowBytes;            // 16,384
-constexpr int kSOff = kWOff + 2 * 1024;           // 18,432
-constexpr int kDummyOff = kSOff + 2 * 256;        // 18,944
-constexpr int kSlotBytes = kDummyOff + 256;       // 19,200
 constexpr int kStages = 6;                        // loads run four steps ahead
 constexpr int kLoadsPerStep = 3;                  // per wave: 2 X + 1 code/scale/dummy
-constexpr int kBTileBytes = BN * 64;              // fp16 B tile: 128 columns x 32
-constexpr int kBOff = kStages * kSlotBytes;       // 115,200
-constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;   // 139,776 B of the 160 KB
+
+// Layout of one workgroup's LDS for NT packed 64-row weight tiles (a 256 x
+// 64 NT output tile).  One ring slot: X (256 rows x 64 B), the codes of one
+// block of the NT packed tiles (NT x 1 KB), their scales (NT x 256 B: a
+// 2-byte load to LDS fills one dword per lane, zero-extended), and 256 B that
+// absorb the extra loads of waves with nothing else to copy.  Behind the
+// ring: three fp16 B tiles (64 NT columns x 32).
+template <int NT>
+struct Cfg {
+    static constexpr int BN = 64 * NT;
+    static constexpr int kWOff = BM * kXRowBytes;                 // 16,384
+    static constexpr int kSOff = kWOff + NT * 1024;
+    static constexpr int kDummyOff = kSOff + NT * 256;
+    static constexpr int kSlotBytes = kDummyOff + 256;
+    static constexpr int kBTileBytes = BN * 64;
+    static constexpr int kBOff = kStages * kSlotBytes;
+    static constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;     // NT 2: 139,776; NT 3: 159,744
+    static constexpr int kCPitch = BN + 8;                        // epilogue row pitch (floats)
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
+    static_assert(128 * kCPitch * 4 <= kLdsBytes, "epilogue staging");
+    static_assert(NT <= 4, "one code or scale load per wave");
+};
+
 // Output tiles below which K is split across workgroups, and the workgroups
 // a split aims for.
 constexpr int kSplitBelowTiles = 128;
 constexpr int kSplitTargetWgs = 256;
 
-struct GemmArgs {
+// One weight matrix of a launch.  Every matrix of a launch shares X, M and
+// K; its workgroups are wg0 .. wg0 + tiles_m * tiles_n * S - 1.
+struct GemmMat {
     const uint8_t* codes;     // code plane (tiled layout)
     const uint16_t* scales;   // scale plane (tiled layout)
-    const _Float16* X;        // M x K row-major
     float* out;               // Y (S == 1) or S partial M x N slices
-    int32_t M, N, K, nu;      // nu = K / 32
-    int32_t tiles_m, tiles_n, S, us;   // us: blocks per K slice
+    int32_t N, tiles_n, wg0, pad;
+};
+
+struct GemmArgs {
+    GemmMat mat[kMaxGemmGroup];
+    const _Float16* X;        // M x K row-major
+    int32_t count;            // matrices
+    int32_t M, K, nu;         // nu = K / 32
+    int32_t tiles_m, S, us;   // us: blocks per K slice
     int32_t remap;            // 1: XCD-aware workgroup order
-    int32_t pad;
 };
 
 __device__ __forceinline__ uint32_t bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -110,16 +128,24 @@ __device__ __forceinline__ void lds_barrier() {
 // of this wave are outstanding (lgkm and exp counters left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
 
+template <int NT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a) {
+    using C = Cfg<NT>;
+    constexpr int BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-    // Work item: M tile fastest, then N tile, then K slice.
+    // Work item: matrix, then (inside it) M tile fastest, then N tile, then
+    // K slice.
     int L = blockIdx.x;
     if (a.remap) L = (L % 8) * int(gridDim.x / 8) + L / 8;
-    const int tm = L % a.tiles_m;
-    const int rest = L / a.tiles_m;
-    const int tn = rest % a.tiles_n;
-    const int ks = rest / a.tiles_n;
+    int mi = 0;
+    for (int i = 1; i < a.count; ++i) mi += L >= a.mat[i].wg0 ? 1 : 0;
+    const GemmMat& G = a.mat[mi];
+    const int local = L - G.wg0;
+    const int tm = local % a.tiles_m;
+    const int rest = local / a.tiles_m;
+    const int tn = rest % G.tiles_n;
+    const int ks = rest / G.tiles_n;
     const int m0 = tm * BM;
     const int u0 = ks * a.us;
     const int nst = min(a.nu, u0 + a.us) - u0;   // steps (blocks) of this slice
@@ -129,16 +155,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5;
-    const int tiles_b = (a.N + kTileRows - 1) / kTileRows;
+    const int tiles_b = (G.N + kTileRows - 1) / kTileRows;
 
     // ---- copy ring.  Per step each wave issues kLoadsPerStep loads:
     //   X: wave w covers rows 32 w .. +32 in two 1 KB loads; lane s of load
     //      i fills row 32 w + 16 i + s / 4, physical chunk s % 4, i.e.
     //      logical chunk (s % 4) ^ ((row >> 2) & 3).
-    //   waves 0-1: the block's codes of packed tile 2 tn + w (lane s: row s,
-    //      clamped into the tile); waves 2-3: its scales; waves 4-7: a spare
-    //      load of scales into the slot's dummy area (keeps the per-wave
-    //      count uniform for the wait).
+    //   waves 0 .. NT-1: the block's codes of packed tile NT tn + w (lane s:
+    //      row s, clamped into the tile); waves NT .. 2 NT - 1: its scales;
+    //      the other waves: a spare load of scales into the slot's dummy
+    //      area (keeps the per-wave count uniform for the wait).
     uint32_t xo[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -146,14 +172,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
         const int c = (lane & 3) ^ ((row >> 2) & 3);
         xo[i] = uint32_t(min(m0 + row, a.M - 1)) * uint32_t(a.K) * 2u + uint32_t(c) * 16u;
     }
-    const int lt = wave & 1;
-    const int ltb = min(tn * 2 + lt, tiles_b - 1);
-    const int lnr = min(kTileRows, a.N - ltb * kTileRows);
-    const uint8_t* lcode = a.codes + size_t(ltb) * kTileRows * size_t(a.nu) * 16;
-    const uint16_t* lscale = a.scales + size_t(ltb) * kTileRows * size_t(a.nu);
+    const int lt = wave < NT ? wave : (wave < 2 * NT ? wave - NT : 0);
+    const int ltb = min(tn * NT + lt, tiles_b - 1);
+    const int lnr = min(kTileRows, G.N - ltb * kTileRows);
+    const uint8_t* lcode = G.codes + size_t(ltb) * kTileRows * size_t(a.nu) * 16;
+    const uint16_t* lscale = G.scales + size_t(ltb) * kTileRows * size_t(a.nu);
     const uint32_t lrow = uint32_t(min(lane, lnr - 1));
     auto issue = [&](int st) {   // loads of step st into slot st % kStages
-        uint8_t* slot = lds + (st % kStages) * kSlotBytes;
+        uint8_t* slot = lds + (st % kStages) * C::kSlotBytes;
         const int ub = u0 + st;
         const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.X) + size_t(ub) * 64;
 #pragma unroll
@@ -162,41 +188,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
                 (const __attribute__((address_space(1))) void*)(xb + xo[i]),
                 (__attribute__((address_space(3))) void*)(slot + (2 * wave + i) * 1024), 16, 0, 0);
         const size_t e = size_t(ub) * size_t(lnr) + lrow;
-        if (wave < 2)
+        if (wave < NT)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(lcode + e * 16),
-                (__attribute__((address_space(3))) void*)(slot + kWOff + lt * 1024), 16, 0, 0);
+                (__attribute__((address_space(3))) void*)(slot + C::kWOff + lt * 1024), 16, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(lscale + e),
-                (__attribute__((address_space(3))) void*)(slot + (wave < 4 ? kSOff + lt * 256 : kDummyOff)), 2, 0, 0);
+                (__attribute__((address_space(3))) void*)(slot + (wave < 2 * NT ? C::kSOff + lt * 256 : C::kDummyOff)),
+                2, 0, 0);
     };
 
-    // ---- unpack: thread t turns 8 weights of column n = t / 4 into one
+    // ---- unpack: task t turns 8 weights of column n = t / 4 into one
     // 16-byte chunk of the fp16 B tile: part p = t % 4 takes elements
     // 8p .. 8p + 7 of the block, i.e. the low (p < 2) or high (p >= 2)
-    // nibbles of code bytes 8 (p % 2) .. 8 (p % 2) + 7 (GGUF order).
-    const int un = tid >> 2, up = tid & 3;
-    const uint32_t uc_off = uint32_t(kWOff + (un >> 6) * 1024 + (un & 63) * 16 + 8 * (up & 1));
-    const uint32_t us_off = uint32_t(kSOff + (un >> 6) * 256 + (un & 63) * 4);
-    const uint32_t ub_off = sw_off(un, up);
+    // nibbles of code bytes 8 (p % 2) .. 8 (p % 2) + 7 (GGUF order).  There
+    // are 4 BN tasks: thread t takes task t, and for NT = 3 also task
+    // 512 + t % 256 (waves 4-7 repeat the tasks of waves 0-3, writing the
+    // same bytes): no branch, so the compiler can interleave the unpacking
+    // with the matrix instructions.
+    constexpr int kTasks = NT == 2 ? 1 : 2;
+    static_assert(NT == 2 || NT == 3, "task split");
+    uint32_t uc_off[kTasks], us_off[kTasks], ub_off[kTasks];
+    int ush[kTasks];
+#pragma unroll
+    for (int q = 0; q < kTasks; ++q) {
+        const int t = q == 0 ? tid : kThreads + (tid & 255);
+        const int un = t >> 2, up = t & 3;
+        uc_off[q] = uint32_t(C::kWOff + (un >> 6) * 1024 + (un & 63) * 16 + 8 * (up & 1));
+        us_off[q] = uint32_t(C::kSOff + (un >> 6) * 256 + (un & 63) * 4);
+        ub_off[q] = sw_off(un, up);
+        ush[q] = (up >> 1) * 4;
+    }
     auto unpack = [&](const uint8_t* slot, uint8_t* btile) {
-        const u32x2 c = *reinterpret_cast<const u32x2*>(slot + uc_off);
-        const uint16_t d = *reinterpret_cast<const uint16_t*>(slot + us_off);
-        const _Float16 dh = __builtin_bit_cast(_Float16, d);
-        const half2_t dd = {dh, dh};
-        const int sh = (up >> 1) * 4;
-        const uint32_t n0 = (c.x >> sh) & 0x0F0F0F0Fu, n1 = (c.y >> sh) & 0x0F0F0F0Fu;
-        const u32x4 v = {w2(n0, 0x04010400u, dd), w2(n0, 0x04030402u, dd), w2(n1, 0x04010400u, dd),
-                         w2(n1, 0x04030402u, dd)};
-        *reinterpret_cast<u32x4*>(btile + ub_off) = v;
+#pragma unroll
+        for (int q = 0; q < kTasks; ++q) {
+            const u32x2 c = *reinterpret_cast<const u32x2*>(slot + uc_off[q]);
+            const uint16_t d = *reinterpret_cast<const uint16_t*>(slot + us_off[q]);
+            const _Float16 dh = __builtin_bit_cast(_Float16, d);
+            const half2_t dd = {dh, dh};
+            const uint32_t n0 = (c.x >> ush[q]) & 0x0F0F0F0Fu, n1 = (c.y >> ush[q]) & 0x0F0F0F0Fu;
+            const u32x4 v = {w2(n0, 0x04010400u, dd), w2(n0, 0x04030402u, dd), w2(n1, 0x04010400u, dd),
+                             w2(n1, 0x04030402u, dd)};
+            *reinterpret_cast<u32x4*>(btile + ub_off[q]) = v;
+        }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][NT];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -210,19 +252,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
     // may be in flight, and st + 5 is issued (clamped to the last step: past
     // the end the copy lands in a slot nobody reads, so every step issues the
     // same number of loads and the wait count is a constant).
-    auto slot_of = [&](int st) { return lds + (st % kStages) * kSlotBytes; };
-    auto btile_of = [&](int st) { return lds + kBOff + (st % 3) * kBTileBytes; };
-    half8_t af[2][2], bf[2][2];   // [sub-step][block] of the next step to multiply
+    auto slot_of = [&](int st) { return lds + (st % kStages) * C::kSlotBytes; };
+    auto btile_of = [&](int st) { return lds + C::kBOff + (st % 3) * C::kBTileBytes; };
+    // Fragment offsets of this lane: A rows wm 64 + 32 i + lane % 32, B
+    // columns wn 32 NT + 32 j + lane % 32, chunk 2 s + h.  Blocks 32 rows
+    // apart keep the row's swizzle bits, so block i (j) is 2 KB i (j) further:
+    // an immediate offset of the LDS read.
+    const uint32_t a_off[2] = {sw_off(wm * 64 + (lane & 31), h), sw_off(wm * 64 + (lane & 31), 2 + h)};
+    const uint32_t b_off[2] = {sw_off(wn * 32 * NT + (lane & 31), h), sw_off(wn * 32 * NT + (lane & 31), 2 + h)};
+    half8_t af[2][2], bf[2][NT];   // [sub-step][block] of the next step to multiply
     auto read_frags = [&](int st) {
         const uint8_t* slot = slot_of(st);
         const uint8_t* bt = btile_of(st);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[s][i] = *reinterpret_cast<const half8_t*>(slot + sw_off(wm * 64 + i * 32 + (lane & 31), 2 * s + h));
-                bf[s][i] = *reinterpret_cast<const half8_t*>(bt + sw_off(wn * 64 + i * 32 + (lane & 31), 2 * s + h));
-            }
+            for (int i = 0; i < 2; ++i) af[s][i] = *reinterpret_cast<const half8_t*>(slot + a_off[s] + i * 2048);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) bf[s][j] = *reinterpret_cast<const half8_t*>(bt + b_off[s] + j * 2048);
+        }
     };
     if (nst > 0) {
 #pragma unroll
@@ -239,35 +287,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
         lds_barrier();
         issue(min(st + kStages - 1, nst - 1));
         unpack(slot_of(st + 2), btile_of(st + 2));   // past the last step: unused data
-        half8_t a0[2][2], b0[2][2];
+        half8_t a0[2][2], b0[2][NT];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                a0[s][i] = af[s][i];
-                b0[s][i] = bf[s][i];
-            }
+            for (int i = 0; i < 2; ++i) a0[s][i] = af[s][i];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) b0[s][j] = bf[s][j];
+        }
         read_frags(st + 1);                          // past the last step: unused data
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[s][i], b0[s][j], acc[i][j], 0, 0, 0);
     }
 
     // ---- epilogue: the tile goes through LDS in two halves of 128 rows so
-    // global stores are whole 512-byte rows, 16 bytes per lane.  32x32
-    // accumulator layout: register r of lane l is row 8 (r / 4) + 4 (l / 32)
-    // + r % 4, column l % 32.  Row pitch 136 floats: the two half waves
-    // (rows 4 apart) write disjoint banks.
-    constexpr int kCPitch = BN + 8;
+    // global stores are whole rows, 16 bytes per lane.  32x32 accumulator
+    // layout: register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column l % 32.  Row pitch BN + 8 floats: the two half waves (rows 4
+    // apart) write disjoint banks.
+    constexpr int kCPitch = C::kCPitch;
+    constexpr int kChunks = BN / 4;                  // 16-byte chunks per row
     float* cst = reinterpret_cast<float*>(lds);
-    float* out = a.out + size_t(ks) * size_t(a.M) * size_t(a.N);
+    float* out = G.out + size_t(ks) * size_t(a.M) * size_t(G.N);
     const int n0 = tn * BN;
-    const int col = (tid & 31) * 4;
-    const bool full = m0 + BM <= a.M && n0 + BN <= a.N && (a.N & 3) == 0;
+    const bool full = m0 + BM <= a.M && n0 + BN <= G.N && (G.N & 3) == 0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         __syncthreads();
@@ -275,25 +323,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NT; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = (wm & 1) * 64 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                        cst[row * kCPitch + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][r];
+                        cst[row * kCPitch + wn * 32 * NT + j * 32 + (lane & 31)] = acc[i][j][r];
                     }
         }
         __syncthreads();
-#pragma unroll 4
-        for (int k = 0; k < 8; ++k) {
-            const int row = (tid >> 5) + 16 * k;
+        for (int idx = tid; idx < 128 * kChunks; idx += kThreads) {
+            const int row = idx / kChunks;
+            const int col = (idx - row * kChunks) * 4;
             const f32x4 v = *reinterpret_cast<const f32x4*>(cst + row * kCPitch + col);
             const int m = m0 + half * 128 + row;
             if (full) {
-                *reinterpret_cast<f32x4*>(out + size_t(m) * size_t(a.N) + n0 + col) = v;
+                *reinterpret_cast<f32x4*>(out + size_t(m) * size_t(G.N) + n0 + col) = v;
             } else if (m < a.M) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (n0 + col + e < a.N) out[size_t(m) * size_t(a.N) + n0 + col + e] = v[e];
+                    if (n0 + col + e < G.N) out[size_t(m) * size_t(G.N) + n0 + col + e] = v[e];
             }
         }
     }
@@ -317,30 +365,76 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
     }
 }
 
+// Tile width and K split of a launch of `count` matrices that share X:
+// NT packed 64-row tiles per workgroup (2 or 3) and S K slices (single
+// matrices with few output tiles only).  One workgroup fits a CU's LDS, so
+// the launch takes ceil(workgroups / CUs) rounds of NT x (blocks per slice)
+// steps' work each.  The wide tile is taken only where it needs no K split
+// and does less of that work (a fused FFN gate + up at M = 512: 232
+// workgroups in one round instead of 344 in two); with a split its partial
+// sums cost more than it gained (measured on the 11008 x 2048 matrix alone).
 struct Plan {
-    int tiles_m, tiles_n, S, us;
+    int nt, tiles_m, S, us;
+    int64_t wgs;
 };
 
-Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
+Plan plan_for(int nt, int64_t M, const int64_t* N, int count, int64_t K) {
     Plan p;
+    p.nt = nt;
     p.tiles_m = int((M + BM - 1) / BM);
-    p.tiles_n = int((N + BN - 1) / BN);
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) tiles += int64_t(p.tiles_m) * ((N[i] + 64 * nt - 1) / (64 * nt));
     const int nu = int(K / 32);
-    const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
     int S = 1;
-    if (tiles < kSplitBelowTiles) S = int(std::max<int64_t>(1, kSplitTargetWgs / tiles));
+    if (count == 1 && tiles < kSplitBelowTiles) S = int(std::max<int64_t>(1, kSplitTargetWgs / tiles));
     S = std::min(S, std::max(1, nu / 16));   // at least 16 blocks (steps) per slice
     const int us = (nu + S - 1) / S;
     p.us = us;
     p.S = (nu + us - 1) / us;                // no empty slice
+    p.wgs = tiles * p.S;
     return p;
+}
+
+Plan plan_gemm(int64_t M, const int64_t* N, int count, int64_t K, int cus) {
+#ifdef LQ_GEMM_NT_ONLY
+    return plan_for(LQ_GEMM_NT_ONLY, M, N, count, K);
+#endif
+    const Plan p2 = plan_for(2, M, N, count, K), p3 = plan_for(3, M, N, count, K);
+    if (p3.S > 1) return p2;
+    const int64_t c = std::max(cus, 1);
+    const int64_t w2 = (p2.wgs + c - 1) / c * 2 * p2.us, w3 = (p3.wgs + c - 1) / c * 3 * p3.us;
+    return w3 < w2 ? p3 : p2;
+}
+
+template <int NT>
+hipError_t launch_nt(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    // The ring needs more than the default 64 KB of dynamic LDS: raise the
+    // kernel's limit once per device.
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static std::atomic<bool> lds_ok[64];
+    if (!lds_ok[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_q4_0_kernel<NT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<NT>::kLdsBytes);
+        if (e != hipSuccess) return e;
+        lds_ok[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(gemm_q4_0_kernel<NT>, dim3(unsigned(grid)), dim3(kThreads), Cfg<NT>::kLdsBytes, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const Plan p = plan_gemm(M, N, K);
-    return p.S > 1 ? size_t(p.S) * size_t(M) * size_t(N) * sizeof(float) : 0;
+    // Whichever tile width the launch picks (that depends on the CU count).
+    size_t need = 0;
+    for (int nt = 2; nt <= 3; ++nt) {
+        const Plan p = plan_for(nt, M, &N, 1, K);
+        if (p.S > 1) need = std::max(need, size_t(p.S) * size_t(M) * size_t(N) * sizeof(float));
+    }
+    return need;
 }
 
 hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipStream_t stream) {
@@ -349,43 +443,37 @@ hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_q4_0(const void* W, const void* X, float* Y, int64_t M, int64_t N,
-                            int64_t K, void* ws, size_t, int, hipStream_t stream) {
-    const Plan p = plan_gemm(M, N, K);
-    GemmArgs a;
-    a.codes = static_cast<const uint8_t*>(W);
-    a.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(W) +
-                                                 align256(code_plane_bytes(kQ4_0, N, K)));
+hipError_t launch_gemm_q4_0(const void* const* W, float* const* Y, const int64_t* N, int count, const void* X,
+                            int64_t M, int64_t K, void* ws, int cus, hipStream_t stream) {
+    if (count < 1 || count > kMaxGemmGroup) return hipErrorInvalidValue;
+    const Plan p = plan_gemm(M, N, count, K, cus);
+    GemmArgs a = {};
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
+        GemmMat& g = a.mat[i];
+        g.codes = static_cast<const uint8_t*>(W[i]);
+        g.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(W[i]) +
+                                                     align256(code_plane_bytes(kQ4_0, N[i], K)));
+        g.out = p.S > 1 ? static_cast<float*>(ws) : Y[i];
+        g.N = int32_t(N[i]);
+        g.tiles_n = int32_t((N[i] + 64 * p.nt - 1) / (64 * p.nt));
+        g.wg0 = int32_t(wgs);
+        g.pad = 0;
+        wgs += int64_t(p.tiles_m) * g.tiles_n * p.S;
+    }
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
     a.X = static_cast<const _Float16*>(X);
-    a.out = p.S > 1 ? static_cast<float*>(ws) : Y;
+    a.count = count;
     a.M = int32_t(M);
-    a.N = int32_t(N);
     a.K = int32_t(K);
     a.nu = int32_t(K / 32);
     a.tiles_m = p.tiles_m;
-    a.tiles_n = p.tiles_n;
     a.S = p.S;
     a.us = p.us;
-    const int64_t grid = int64_t(p.tiles_m) * p.tiles_n * p.S;
-    a.remap = (grid % 8 == 0) ? 1 : 0;
-    a.pad = 0;
-    // The ring needs more than the default 64 KB of dynamic LDS: raise the
-    // kernel's limit once per device.
-    int dev = 0;
-    hipError_t e0 = hipGetDevice(&dev);
-    if (e0 != hipSuccess) return e0;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    static std::atomic<bool> lds_ok[64];
-    if (!lds_ok[dev].load(std::memory_order_acquire)) {
-        e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_q4_0_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e0 != hipSuccess) return e0;
-        lds_ok[dev].store(true, std::memory_order_release);
-    }
-    hipLaunchKernelGGL(gemm_q4_0_kernel, dim3(unsigned(grid)), dim3(kThreads), kLdsBytes, stream, a);
-    hipError_t e = hipGetLastError();
+    a.remap = (wgs % 8 == 0) ? 1 : 0;
+    const hipError_t e = p.nt == 3 ? launch_nt<3>(a, wgs, stream) : launch_nt<2>(a, wgs, stream);
     if (e != hipSuccess || p.S == 1) return e;
-    return launch_splitk_reduce(static_cast<const float*>(ws), Y, size_t(M) * size_t(N), p.S, stream);
+    return launch_splitk_reduce(static_cast<const float*>(ws), Y[0], size_t(M) * size_t(N[0]), p.S, stream);
 }
 
 }  // namespace lq

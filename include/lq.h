@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 4
+#define LQ_ABI_VERSION 5
 
 typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2 } lq_fmt;
 /* Activation and source dtypes.  LQ_BF16 is accepted only as the source of
@@ -247,6 +247,31 @@ size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 lq_status lq_gemm(int32_t fmt, const void* W, const void* X, int32_t xdt,
                   float* Y, int64_t M, int64_t N, int64_t K,
                   void* ws, size_t ws_bytes, void* stream);
+
+/* One weight matrix of lq_gemm_batch: W packed N x K, Y M x N fp32. */
+typedef struct lq_gemm_desc {
+    const void* W;
+    float* Y;
+    int64_t N;
+} lq_gemm_desc;
+
+/* Most matrices one lq_gemm_batch call takes. */
+#define LQ_GEMM_MAX_GROUP 4
+
+/* lq_gemm over `count` weight matrices (1 <= count <= LQ_GEMM_MAX_GROUP) of
+ * one format that share X, M and K, e.g. the gate and up projections of one
+ * FFN over the same prompt chunk: for each descriptor, Y = X W^T as lq_gemm
+ * computes it (the same fp16 weight tile and products, with the same
+ * accuracy; the same bits whenever lq_gemm needs no workspace for that matrix
+ * alone, i.e. does not split its K).  LQ_Q4_0 runs all of them in one
+ * kernel launch, so their output tiles fill the GPU together; LQ_Q8_0 and
+ * LQ_I8B64 run one launch per matrix, in order.  descs: HOST array, read
+ * during the call only; everything is validated before anything is enqueued.
+ * ws / ws_bytes: a workspace of the largest lq_gemm_workspace_bytes() over
+ * the descriptors suffices (an LQ_Q4_0 call with count > 1 needs none). */
+lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int64_t K,
+                        const lq_gemm_desc* descs, int32_t count,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Route by token count, after the "oxinfer" page's rule that GPU matmul
  * kernels take only prompt-sized work ("Platforms and accelerators": t >= 16

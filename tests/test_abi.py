@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 4
+    assert lq.lq_abi_version() == 5
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -94,6 +94,21 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_gemm(0, A16, A16 + 2, 1, A16, 16, 32, 32, None, 0, None) == ALIGN
     assert g.lq_gemm(0, A16, A16, 7, A16, 16, 32, 32, None, 0, None) == DTYPE
     assert g.lq_matmul(0, A16, A16, 1, A16, 0, 32, 32, None, 0, None) == SHAPE
+    # grouped gemm: count, descriptor and per-matrix validation
+    gd = (lq.lq_gemm_desc * 5)()
+    for i in range(5):
+        gd[i] = lq.lq_gemm_desc(A16, A16, 64)
+    assert g.lq_gemm_batch(0, A16, 1, 16, 64, None, 1, None, 0, None) == ARG
+    assert g.lq_gemm_batch(0, A16, 1, 16, 64, gd, 0, None, 0, None) == ARG
+    assert g.lq_gemm_batch(0, A16, 1, 16, 64, gd, lq.LQ_GEMM_MAX_GROUP + 1, None, 0, None) == ARG
+    assert g.lq_gemm_batch(0, A16, 0, 16, 64, gd, 2, None, 0, None) == UNSUP     # fp32 X
+    assert g.lq_gemm_batch(0, A16 + 2, 1, 16, 64, gd, 2, None, 0, None) == ALIGN
+    gd[1] = lq.lq_gemm_desc(A16, A16, 0)
+    assert g.lq_gemm_batch(0, A16, 1, 16, 64, gd, 2, None, 0, None) == SHAPE
+    gd[1] = lq.lq_gemm_desc(A16 + 4, A16, 64)
+    assert g.lq_gemm_batch(0, A16, 1, 16, 64, gd, 2, None, 0, None) == ALIGN
+    gd[1] = lq.lq_gemm_desc(A16, None, 64)
+    assert g.lq_gemm_batch(0, A16, 1, 16, 64, gd, 2, None, 0, None) == ARG
     # multi-token GEMV: fp16 activations, 1 <= M <= 16
     assert g.lq_gemv_multi(0, A16, A16, 0, A16, 4, 64, 32, None) == UNSUP
     assert g.lq_gemv_multi(0, A16, A16, 1, A16, 0, 64, 32, None) == SHAPE
