@@ -440,8 +440,9 @@ lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, 
 }
 
 namespace {
-// Q4_0: the LDS-tile GEMM; Q8_0 and int8 block-64: the register-fragment one.
-bool use_lds_tile_gemm(int32_t fmt) { return fmt == LQ_Q4_0; }
+// Q4_0 and Q8_0: the LDS-tile GEMM (fp16 weight tiles); int8 block-64 (fp32
+// scales, not an fp16 tile): the register-fragment one.
+bool use_lds_tile_gemm(int32_t fmt) { return fmt == LQ_Q4_0 || fmt == LQ_Q8_0; }
 
 size_t gemm_ws(int32_t fmt, int64_t M, int64_t N, int64_t K) {
     return use_lds_tile_gemm(fmt) ? lq::gemm_workspace_bytes(M, N, K) : lq::prefill_workspace_bytes(M, N, K);
@@ -495,7 +496,7 @@ lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int6
             Y[i] = descs[i].Y;
             N[i] = descs[i].N;
         }
-        const hipError_t e = lq::launch_gemm_q4_0(W, Y, N, count, X, M, K, ws, cus, s);
+        const hipError_t e = lq::launch_gemm_tile(fmt, W, Y, N, count, X, M, K, ws, cus, s);
         return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
     }
     for (int i = 0; i < count; ++i) {

@@ -50,29 +50,33 @@ constexpr int BM = 256;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXRowBytes = 64;
-constexpr int kStages = 6;                        // loads run four steps ahead
-constexpr int kLoadsPerStep = 3;                  // per wave: 2 X + 1 code/scale/dummy
 
-// Layout of one workgroup's LDS for NT packed 64-row weight tiles (a 256 x
-// 64 NT output tile).  One ring slot: X (256 rows x 64 B), the codes of one
-// block of the NT packed tiles (NT x 1 KB), their scales (NT x 256 B: a
+// Layout of one workgroup's LDS for format FMT (Q4_0 or Q8_0) and NT packed
+// 64-row weight tiles (a 256 x 64 NT output tile).  One ring slot: X (256
+// rows x 64 B), the codes of one block of the NT packed tiles (P = 1 or 2
+// parts of 1 KB each per tile, in packed order), their scales (NT x 256 B: a
 // 2-byte load to LDS fills one dword per lane, zero-extended), and 256 B that
 // absorb the extra loads of waves with nothing else to copy.  Behind the
-// ring: three fp16 B tiles (64 NT columns x 32).
-template <int NT>
+// ring: three fp16 B tiles (64 NT columns x 32).  Each wave issues two X
+// loads and kOthers code / scale / spare loads per step.
+template <int FMT, int NT>
 struct Cfg {
+    static constexpr int P = FMT == kQ8_0 ? 2 : 1;                // 16-byte code parts per unit
     static constexpr int BN = 64 * NT;
+    static constexpr int kStages = (P == 2 && NT == 3) ? 5 : 6;   // copies run kStages - 2 steps ahead
+    static constexpr int kOthers = (NT * P + NT + kWaves - 1) / kWaves;
+    static constexpr int kLoadsPerStep = 2 + kOthers;
     static constexpr int kWOff = BM * kXRowBytes;                 // 16,384
-    static constexpr int kSOff = kWOff + NT * 1024;
+    static constexpr int kSOff = kWOff + NT * P * 1024;
     static constexpr int kDummyOff = kSOff + NT * 256;
     static constexpr int kSlotBytes = kDummyOff + 256;
     static constexpr int kBTileBytes = BN * 64;
     static constexpr int kBOff = kStages * kSlotBytes;
-    static constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;     // NT 2: 139,776; NT 3: 159,744
+    static constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;     // <= 159,744
     static constexpr int kCPitch = BN + 8;                        // epilogue row pitch (floats)
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
     static_assert(128 * kCPitch * 4 <= kLdsBytes, "epilogue staging");
-    static_assert(NT <= 4, "one code or scale load per wave");
+    static_assert(kStages >= 5, "the unpack needs step st + 2 landed");
 };
 
 // Output tiles below which K is split across workgroups, and the workgroups
@@ -107,6 +111,14 @@ __device__ __forceinline__ uint32_t w2(uint32_t v, uint32_t sel, half2_t dd) {
     return bits((as_half2(__builtin_amdgcn_perm(0x64646464u, v, sel)) - off) * dd);
 }
 
+// Two fp16 weights RN_fp16(c * d) from two sign-flipped int8 codes (bytes
+// `sel` of v): under 0x64 a byte u is the fp16 value 1024 + u, and
+// u - 128 = c.
+__device__ __forceinline__ uint32_t w8(uint32_t v, uint32_t sel, half2_t dd) {
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return bits((as_half2(__builtin_amdgcn_perm(0x64646464u, v, sel)) - off) * dd);
+}
+
 // LDS byte offset of 16-byte chunk `chunk` (0-3) of a 64-byte row (an X row
 // or a B column).  XORing the chunk with bits 2-3 of the row makes the 16
 // lanes of one LDS cycle (64 banks) hit 16 distinct (row % 4, chunk) slots
@@ -128,9 +140,12 @@ __device__ __forceinline__ void lds_barrier() {
 // of this wave are outstanding (lgkm and exp counters left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
 
-template <int NT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a) {
-    using C = Cfg<NT>;
+template <int FMT, int NT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a) {
+    using C = Cfg<FMT, NT>;
+    constexpr int P = C::P;
+    constexpr int kStages = C::kStages;
+    constexpr int kLoadsPerStep = C::kLoadsPerStep;
     constexpr int BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -161,10 +176,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
     //   X: wave w covers rows 32 w .. +32 in two 1 KB loads; lane s of load
     //      i fills row 32 w + 16 i + s / 4, physical chunk s % 4, i.e.
     //      logical chunk (s % 4) ^ ((row >> 2) & 3).
-    //   waves 0 .. NT-1: the block's codes of packed tile NT tn + w (lane s:
-    //      row s, clamped into the tile); waves NT .. 2 NT - 1: its scales;
-    //      the other waves: a spare load of scales into the slot's dummy
-    //      area (keeps the per-wave count uniform for the wait).
+    //   kOthers more, numbered q = w + 8 k: q < NT P: part q % P of the
+    //      block's codes of packed tile NT tn + q / P (lane s: row s, clamped
+    //      into the tile); then NT scale loads; the rest a spare load of
+    //      scales into the slot's dummy area (keeps the per-wave count
+    //      uniform for the wait).
     uint32_t xo[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -172,41 +188,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
         const int c = (lane & 3) ^ ((row >> 2) & 3);
         xo[i] = uint32_t(min(m0 + row, a.M - 1)) * uint32_t(a.K) * 2u + uint32_t(c) * 16u;
     }
-    const int lt = wave < NT ? wave : (wave < 2 * NT ? wave - NT : 0);
-    const int ltb = min(tn * NT + lt, tiles_b - 1);
-    const int lnr = min(kTileRows, G.N - ltb * kTileRows);
-    const uint8_t* lcode = G.codes + size_t(ltb) * kTileRows * size_t(a.nu) * 16;
-    const uint16_t* lscale = G.scales + size_t(ltb) * kTileRows * size_t(a.nu);
-    const uint32_t lrow = uint32_t(min(lane, lnr - 1));
+    constexpr int kOthers = C::kOthers;
+    const uint8_t* osrc[kOthers];   // per-lane source of the step-0 block
+    uint32_t ostep[kOthers];        // source bytes per step
+    uint32_t odst[kOthers];         // LDS offset inside the slot
+    int osize[kOthers];             // 16 (codes) or 2 (scales)
+#pragma unroll
+    for (int k = 0; k < kOthers; ++k) {
+        const int q = wave + kWaves * k;
+        const bool code = q < NT * P;
+        const int t = code ? q / P : (q < NT * P + NT ? q - NT * P : 0);
+        const int ltb = min(tn * NT + t, tiles_b - 1);
+        const int lnr = min(kTileRows, G.N - ltb * kTileRows);
+        const uint32_t lrow = uint32_t(min(lane, lnr - 1));
+        if (code) {
+            osrc[k] = G.codes + size_t(ltb) * kTileRows * size_t(a.nu) * P * 16 +
+                      (size_t(u0) * P + size_t(q % P)) * size_t(lnr) * 16 + lrow * 16;
+            ostep[k] = uint32_t(P * lnr * 16);
+            odst[k] = uint32_t(C::kWOff + q * 1024);
+            osize[k] = 16;
+        } else {
+            osrc[k] = reinterpret_cast<const uint8_t*>(G.scales + size_t(ltb) * kTileRows * size_t(a.nu) +
+                                                       size_t(u0) * lnr + lrow);
+            ostep[k] = uint32_t(lnr * 2);
+            odst[k] = uint32_t(q < NT * P + NT ? C::kSOff + t * 256 : C::kDummyOff);
+            osize[k] = 2;
+        }
+    }
     auto issue = [&](int st) {   // loads of step st into slot st % kStages
         uint8_t* slot = lds + (st % kStages) * C::kSlotBytes;
-        const int ub = u0 + st;
-        const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.X) + size_t(ub) * 64;
+        const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.X) + size_t(u0 + st) * 64;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(xb + xo[i]),
                 (__attribute__((address_space(3))) void*)(slot + (2 * wave + i) * 1024), 16, 0, 0);
-        const size_t e = size_t(ub) * size_t(lnr) + lrow;
-        if (wave < NT)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(lcode + e * 16),
-                (__attribute__((address_space(3))) void*)(slot + C::kWOff + lt * 1024), 16, 0, 0);
-        else
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(lscale + e),
-                (__attribute__((address_space(3))) void*)(slot + (wave < 2 * NT ? C::kSOff + lt * 256 : C::kDummyOff)),
-                2, 0, 0);
+#pragma unroll
+        for (int k = 0; k < kOthers; ++k) {
+            const auto* src = (const __attribute__((address_space(1))) void*)(osrc[k] + size_t(st) * ostep[k]);
+            auto* dst = (__attribute__((address_space(3))) void*)(slot + odst[k]);
+            // The copy size must be an immediate: the 16-byte (codes) or
+            // 2-byte (scales) form, chosen per wave.
+            if (osize[k] == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+            else __builtin_amdgcn_global_load_lds(src, dst, 2, 0, 0);
+        }
     };
 
     // ---- unpack: task t turns 8 weights of column n = t / 4 into one
-    // 16-byte chunk of the fp16 B tile: part p = t % 4 takes elements
-    // 8p .. 8p + 7 of the block, i.e. the low (p < 2) or high (p >= 2)
-    // nibbles of code bytes 8 (p % 2) .. 8 (p % 2) + 7 (GGUF order).  There
-    // are 4 BN tasks: thread t takes task t, and for NT = 3 also task
-    // 512 + t % 256 (waves 4-7 repeat the tasks of waves 0-3, writing the
-    // same bytes): no branch, so the compiler can interleave the unpacking
-    // with the matrix instructions.
+    // 16-byte chunk of the fp16 B tile, elements 8p .. 8p + 7 of the block
+    // (p = t % 4), RN_fp16(w) each.  Q4_0: the low (p < 2) or high (p >= 2)
+    // nibbles of code bytes 8 (p % 2) .. 8 (p % 2) + 7 (GGUF order): under
+    // fp16 exponent 2^10 minus 1032 is q - 8 exactly.  Q8_0: code bytes
+    // 8p .. 8p + 7, sign bit flipped and placed under 0x64: minus 1152 is the
+    // int8 code exactly.  Then one fp16 multiply by d.  There are 4 BN
+    // tasks: thread t takes task t, and for NT = 3 also task 512 + t % 256
+    // (waves 4-7 repeat the tasks of waves 0-3, writing the same bytes): no
+    // branch, so the compiler can interleave the unpacking with the matrix
+    // instructions.
     constexpr int kTasks = NT == 2 ? 1 : 2;
     static_assert(NT == 2 || NT == 3, "task split");
     uint32_t uc_off[kTasks], us_off[kTasks], ub_off[kTasks];
@@ -215,7 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
     for (int q = 0; q < kTasks; ++q) {
         const int t = q == 0 ? tid : kThreads + (tid & 255);
         const int un = t >> 2, up = t & 3;
-        uc_off[q] = uint32_t(C::kWOff + (un >> 6) * 1024 + (un & 63) * 16 + 8 * (up & 1));
+        if constexpr (P == 1)
+            uc_off[q] = uint32_t(C::kWOff + (un >> 6) * 1024 + (un & 63) * 16 + 8 * (up & 1));
+        else
+            uc_off[q] = uint32_t(C::kWOff + ((un >> 6) * 2 + (up >> 1)) * 1024 + (un & 63) * 16 + 8 * (up & 1));
         us_off[q] = uint32_t(C::kSOff + (un >> 6) * 256 + (un & 63) * 4);
         ub_off[q] = sw_off(un, up);
         ush[q] = (up >> 1) * 4;
@@ -227,9 +268,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
             const uint16_t d = *reinterpret_cast<const uint16_t*>(slot + us_off[q]);
             const _Float16 dh = __builtin_bit_cast(_Float16, d);
             const half2_t dd = {dh, dh};
-            const uint32_t n0 = (c.x >> ush[q]) & 0x0F0F0F0Fu, n1 = (c.y >> ush[q]) & 0x0F0F0F0Fu;
-            const u32x4 v = {w2(n0, 0x04010400u, dd), w2(n0, 0x04030402u, dd), w2(n1, 0x04010400u, dd),
-                             w2(n1, 0x04030402u, dd)};
+            u32x4 v;
+            if constexpr (P == 1) {
+                const uint32_t n0 = (c.x >> ush[q]) & 0x0F0F0F0Fu, n1 = (c.y >> ush[q]) & 0x0F0F0F0Fu;
+                v = u32x4{w2(n0, 0x04010400u, dd), w2(n0, 0x04030402u, dd), w2(n1, 0x04010400u, dd),
+                          w2(n1, 0x04030402u, dd)};
+            } else {
+                const uint32_t b0 = c.x ^ 0x80808080u, b1 = c.y ^ 0x80808080u;
+                v = u32x4{w8(b0, 0x04010400u, dd), w8(b0, 0x04030402u, dd), w8(b1, 0x04010400u, dd),
+                          w8(b1, 0x04030402u, dd)};
+            }
             *reinterpret_cast<u32x4*>(btile + ub_off[q]) = v;
         }
     };
@@ -247,11 +295,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
     // st - 1, the fragments of step st + 1 are read, and the weights of step
     // st + 2 are unpacked (B tiles are triple-buffered), so LDS latency and
     // unpacking overlap the matrix instructions instead of following a
-    // barrier.  Copies run three steps ahead of the unpacking: at the top of
-    // step st the loads of steps up to st + 2 have landed, st + 3 and st + 4
-    // may be in flight, and st + 5 is issued (clamped to the last step: past
-    // the end the copy lands in a slot nobody reads, so every step issues the
-    // same number of loads and the wait count is a constant).
+    // barrier.  Copies run kStages - 3 steps ahead of the unpacking: at the
+    // top of step st the loads of steps up to st + 2 have landed, those up to
+    // st + kStages - 2 may be in flight, and st + kStages - 1 is issued
+    // (clamped to the last step: past the end the copy lands in a slot nobody
+    // reads, so every step issues the same number of loads and the wait
+    // count is a constant).
     auto slot_of = [&](int st) { return lds + (st % kStages) * C::kSlotBytes; };
     auto btile_of = [&](int st) { return lds + C::kBOff + (st % 3) * C::kBTileBytes; };
     // Fragment offsets of this lane: A rows wm 64 + 32 i + lane % 32, B
@@ -283,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q4_0_kernel(const GemmArgs a
         read_frags(0);
     }
     for (int st = 0; st < nst; ++st) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStep));   // step st + 2 landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 4) * kLoadsPerStep));   // step st + 2 landed
         lds_barrier();
         issue(min(st + kStages - 1, nst - 1));
         unpack(slot_of(st + 2), btile_of(st + 2));   // past the last step: unused data
@@ -406,8 +455,9 @@ Plan plan_gemm(int64_t M, const int64_t* N, int count, int64_t K, int cus) {
     return w3 < w2 ? p3 : p2;
 }
 
-template <int NT>
-hipError_t launch_nt(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+template <int FMT, int NT>
+hipError_t launch_tile(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    using C = Cfg<FMT, NT>;
     // The ring needs more than the default 64 KB of dynamic LDS: raise the
     // kernel's limit once per device.
     int dev = 0;
@@ -416,12 +466,12 @@ hipError_t launch_nt(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     static std::atomic<bool> lds_ok[64];
     if (!lds_ok[dev].load(std::memory_order_acquire)) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_q4_0_kernel<NT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<NT>::kLdsBytes);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tile_kernel<FMT, NT>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
         if (e != hipSuccess) return e;
         lds_ok[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(gemm_q4_0_kernel<NT>, dim3(unsigned(grid)), dim3(kThreads), Cfg<NT>::kLdsBytes, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<FMT, NT>), dim3(unsigned(grid)), dim3(kThreads), C::kLdsBytes, stream, a);
     return hipGetLastError();
 }
 
@@ -443,9 +493,10 @@ hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_q4_0(const void* const* W, float* const* Y, const int64_t* N, int count, const void* X,
-                            int64_t M, int64_t K, void* ws, int cus, hipStream_t stream) {
+hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, const int64_t* N, int count,
+                            const void* X, int64_t M, int64_t K, void* ws, int cus, hipStream_t stream) {
     if (count < 1 || count > kMaxGemmGroup) return hipErrorInvalidValue;
+    if (fmt != kQ4_0 && fmt != kQ8_0) return hipErrorInvalidValue;
     const Plan p = plan_gemm(M, N, count, K, cus);
     GemmArgs a = {};
     int64_t wgs = 0;
@@ -453,7 +504,7 @@ hipError_t launch_gemm_q4_0(const void* const* W, float* const* Y, const int64_t
         GemmMat& g = a.mat[i];
         g.codes = static_cast<const uint8_t*>(W[i]);
         g.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(W[i]) +
-                                                     align256(code_plane_bytes(kQ4_0, N[i], K)));
+                                                     align256(code_plane_bytes(fmt, N[i], K)));
         g.out = p.S > 1 ? static_cast<float*>(ws) : Y[i];
         g.N = int32_t(N[i]);
         g.tiles_n = int32_t((N[i] + 64 * p.nt - 1) / (64 * p.nt));
@@ -471,7 +522,9 @@ hipError_t launch_gemm_q4_0(const void* const* W, float* const* Y, const int64_t
     a.S = p.S;
     a.us = p.us;
     a.remap = (wgs % 8 == 0) ? 1 : 0;
-    const hipError_t e = p.nt == 3 ? launch_nt<3>(a, wgs, stream) : launch_nt<2>(a, wgs, stream);
+    hipError_t e;
+    if (fmt == kQ4_0) e = p.nt == 3 ? launch_tile<kQ4_0, 3>(a, wgs, stream) : launch_tile<kQ4_0, 2>(a, wgs, stream);
+    else e = p.nt == 3 ? launch_tile<kQ8_0, 3>(a, wgs, stream) : launch_tile<kQ8_0, 2>(a, wgs, stream);
     if (e != hipSuccess || p.S == 1) return e;
     return launch_splitk_reduce(static_cast<const float*>(ws), Y[0], size_t(M) * size_t(N[0]), p.S, stream);
 }

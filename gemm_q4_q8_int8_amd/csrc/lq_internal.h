@@ -185,12 +185,13 @@ hipError_t launch_dequant(int fmt, bool to_f16, const void* W, void* out, int64_
                           int64_t K, hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMM ----
-// Matrices one Q4_0 GEMM launch takes (they share X, M and K).
+// Matrices one tile GEMM launch takes (they share X, M and K).
 constexpr int kMaxGemmGroup = 4;
 // Split-K workspace of a single-matrix launch (0: none).  Launches of
 // several matrices never split K.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_q4_0(const void* const* W, float* const* Y, const int64_t* N, int count,
+// Q4_0 and Q8_0: weights dequantized to fp16 tiles in LDS.
+hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, const int64_t* N, int count,
                             const void* X, int64_t M, int64_t K, void* ws, int num_cus,
                             hipStream_t stream);
 // Y = sum of S partial M x N slices (slice order), for split-K GEMMs.
