@@ -26,8 +26,9 @@
 //     slot past the wave's last unit still loads and computes (its sum is
 //     masked off), since per-slot branches let the compiler sink loads below
 //     the first slot's arithmetic.  Q4_0 (most arithmetic per byte) takes
-//     up to 8 units per batch, Q8_0 2 and int8 block-64 1: with the waves
-//     resident per SIMD, larger batches were measured slower.
+//     up to 8 units per batch, Q8_0 2 and int8 block-64 1 (2 in launches with
+//     few waves): with the waves resident per SIMD, larger batches were
+//     measured slower.
 //   * Q4_0 nibbles become exact fp16 values (q - 8) with one v_and_or_b32
 //     (nibble into an fp16 mantissa under exponent 2^10) and one v_pk_add_f16
 //     per two weights.  fp32 activations: v_fma_mix_f32 multiplies that fp16
@@ -360,20 +361,26 @@ hipError_t launch_unr(int unr, const GemvArgs& a, hipStream_t stream) {
 
 // Batch size of a launch: its waves have at most u units (ceil(ceil(nu / S)
 // / W)); they run in ceil(u / cap) batches of ceil(u / batches) units, so
-// that no batch loads and computes many slots past a wave's last unit.
+// that no batch loads and computes many slots past a wave's last unit.  A
+// launch of fewer than kFewWaves waves (under about four per SIMD: a small
+// matrix on its own, e.g. one decoder layer's q/k/v or o) has too few loads
+// in flight with one-unit batches; it takes batches of at least two units.
+constexpr int64_t kFewWaves = 4096;
 int launch_unroll(int fmt, int waves, const GemvArgs& a) {
     int u = 1;
     for (int i = 0; i < a.count; ++i) {
         const int slice = (a.d[i].nu + a.d[i].S - 1) / a.d[i].S;
         u = max(u, (slice + waves - 1) / waves);
     }
-    const int batches = (u + unroll_cap(fmt) - 1) / unroll_cap(fmt);
+    int cap = unroll_cap(fmt);
+    if (int64_t(a.total_wgs) * waves < kFewWaves) cap = max(cap, 2);
+    const int batches = (u + cap - 1) / cap;
     return (u + batches - 1) / batches;
 }
 
 template <int FMT>
 hipError_t launch_fmt(int xdt, int waves, const GemvArgs& a, hipStream_t stream) {
-    constexpr int CAP = unroll_cap(FMT);
+    constexpr int CAP = unroll_cap(FMT) > 2 ? unroll_cap(FMT) : 2;
     const int unr = launch_unroll(FMT, waves, a);
     if (waves == 16) {
         if (xdt == kF32) return launch_unr<FMT, kF32, 16, CAP>(unr, a, stream);
