@@ -139,17 +139,27 @@ std::vector<int> split_first(const std::vector<int64_t>& S) {
     return ord;
 }
 
-// One grouped GEMV launch: up to kMaxBatch descriptors of one format and
-// activation dtype, K split by split_k.
-lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>& g, int cus,
-                       hipStream_t stream) {
+// One matrix of a GEMV launch: mt rows of K activations in x (row pitch K),
+// mt rows of N outputs in y (row pitch N).
+struct GemvJob {
+    const void* W;
+    const void* x;
+    float* y;
+    int64_t N;
+    int64_t K;
+};
+
+// One grouped GEMV launch: up to kMaxBatch matrices of one format and
+// activation dtype, each over mt tokens (1, or 2 with fp16 activations), K
+// split by split_k.
+lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, int cus, hipStream_t stream) {
     const int n = int(g.size());
     std::vector<int64_t> tiles(n), nu(n), S(n, 1);
     for (int i = 0; i < n; ++i) {
-        tiles[i] = (g[i]->N + lq::kTileRows - 1) / lq::kTileRows;
-        nu[i] = g[i]->K / lq::unit_elems(fmt);
+        tiles[i] = (g[i].N + lq::kTileRows - 1) / lq::kTileRows;
+        nu[i] = g[i].K / lq::unit_elems(fmt);
     }
-    split_k(lq::gemv_min_units(fmt), cus, tiles, nu, std::vector<int64_t>(n, 1), S);
+    split_k(lq::gemv_min_units(fmt), cus, tiles, nu, std::vector<int64_t>(n, mt), S);
     // When every matrix splits K at least LQ_GEMV_WIDE_FROM ways, the launch
     // uses 16-wave workgroups: four of the K slices move inside a workgroup
     // (summed in LDS), leaving fewer or no split-K round trips.
@@ -173,7 +183,7 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
     int64_t wgs = 0, part_off = 0, cnt_off = 0;
     for (int j = 0; j < n; ++j) {
         const int i = ord[j];
-        const lq_gemv_desc& d = *g[i];
+        const GemvJob& d = g[i];
         lq::GemvDesc& o = a.d[j];
         o.codes = static_cast<const uint8_t*>(d.W);
         o.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(fmt, d.N, d.K));
@@ -190,7 +200,7 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
         if (S[i] > 1) {
             o.part = part + part_off;
             o.cnt = cntp + cnt_off;
-            part_off += S[i] * tiles[i] * lq::kTileRows;
+            part_off += S[i] * mt * tiles[i] * lq::kTileRows;
             cnt_off += tiles[i];
         }
         wgs += tiles[i] * S[i];
@@ -198,7 +208,7 @@ lq_status launch_chunk(int fmt, int xdt, const std::vector<const lq_gemv_desc*>&
     }
     a.count = n;
     a.total_wgs = int32_t(wgs);
-    const hipError_t e = lq::launch_gemv(fmt, xdt, waves, a, stream);
+    const hipError_t e = lq::launch_gemv(fmt, xdt, waves, mt, a, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMV launch");
     return LQ_OK;
 }
@@ -370,18 +380,18 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream) 
     std::vector<bool> done(size_t(count), false);
     for (int32_t i = 0; i < count; ++i) {
         if (done[i]) continue;
-        std::vector<const lq_gemv_desc*> chunk;
+        std::vector<GemvJob> chunk;
         for (int32_t j = i; j < count; ++j) {
             if (done[j] || descs[j].fmt != descs[i].fmt || descs[j].xdt != descs[i].xdt) continue;
-            chunk.push_back(&descs[j]);
+            chunk.push_back({descs[j].W, descs[j].x, descs[j].y, descs[j].N, descs[j].K});
             done[j] = true;
             if (chunk.size() == size_t(lq::kMaxBatch)) {
-                LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, chunk, cus, static_cast<hipStream_t>(stream)));
+                LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, static_cast<hipStream_t>(stream)));
                 chunk.clear();
             }
         }
         if (!chunk.empty())
-            LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, chunk, cus, static_cast<hipStream_t>(stream)));
+            LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, static_cast<hipStream_t>(stream)));
     }
     return LQ_OK;
 }
@@ -405,22 +415,37 @@ lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, vo
     for (int32_t i = 0; i < count; ++i) LQ_TRY(check_multi_desc(descs[i], i));
     int cus = 0;
     LQ_TRY(device_cus(&cus));
-    // Group by format, keeping order, in chunks of kMaxBatch.
+    // Group by format and kernel, keeping order, in chunks of kMaxBatch.  Up
+    // to lq::gemv_max_tokens(fmt) tokens run on the single-token GEMV kernel
+    // (a few fp16 dot products per weight on the vector units, still under
+    // the weight stream's time), all descriptors of a launch with the same M;
+    // more tokens take the matrix-core kernel.
+    const auto kernel_of = [](const lq_gemv_multi_desc& d) {
+        return d.M <= lq::gemv_max_tokens(d.fmt) ? d.M : int64_t(0);
+    };
     std::vector<bool> done(size_t(count), false);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
     for (int32_t i = 0; i < count; ++i) {
         if (done[i]) continue;
+        const int64_t kern = kernel_of(descs[i]);
         std::vector<const lq_gemv_multi_desc*> chunk;
+        std::vector<GemvJob> jobs;
         for (int32_t j = i; j < count; ++j) {
-            if (done[j] || descs[j].fmt != descs[i].fmt) continue;
-            chunk.push_back(&descs[j]);
+            if (done[j] || descs[j].fmt != descs[i].fmt || kernel_of(descs[j]) != kern) continue;
             done[j] = true;
+            if (kern == 0) chunk.push_back(&descs[j]);
+            else jobs.push_back({descs[j].W, descs[j].X, descs[j].Y, descs[j].N, descs[j].K});
             if (chunk.size() == size_t(lq::kMaxBatch)) {
-                LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, static_cast<hipStream_t>(stream)));
+                LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, st));
                 chunk.clear();
             }
+            if (jobs.size() == size_t(lq::kMaxBatch)) {
+                LQ_TRY(launch_chunk(descs[i].fmt, LQ_F16, int(kern), jobs, cus, st));
+                jobs.clear();
+            }
         }
-        if (!chunk.empty())
-            LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, static_cast<hipStream_t>(stream)));
+        if (!chunk.empty()) LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, st));
+        if (!jobs.empty()) LQ_TRY(launch_chunk(descs[i].fmt, LQ_F16, int(kern), jobs, cus, st));
     }
     return LQ_OK;
 }

@@ -112,29 +112,42 @@ __device__ __forceinline__ float dot_q4_0_f32(const u32x4 c, cf32_p x) {
     return __builtin_fmaf(s_hi, 0.0625f, s_lo);
 }
 
-// Two fp16 values a.lo, b.lo (ll) or a.hi, b.hi (hh) as one pair.
+// Two fp16 values a.lo, b.lo (ll) or a.hi, b.hi (hh) as one pair.  The
+// activations are wave-uniform and sit in SGPRs: written as a shuffle this is
+// one scalar pack (the shift-and-or form became three scalar ops, and with
+// two tokens the scalar unit, shared by the CU's four SIMDs, was the limit).
 __device__ __forceinline__ half2_t pack_ll(uint32_t a, uint32_t b) {
-    return as_half2((a & 0xFFFFu) | (b << 16));
+    return __builtin_shufflevector(as_half2(a), as_half2(b), 0, 2);
 }
 __device__ __forceinline__ half2_t pack_hh(uint32_t a, uint32_t b) {
-    return as_half2((a >> 16) | (b & 0xFFFF0000u));
+    uint32_t r;
+    asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
+    return as_half2(r);
 }
 
-// Same sum with fp16 activations: x holds pairs (x_2i, x_2i+1).
-__device__ __forceinline__ float dot_q4_0_f16(const u32x4 c, cu32_p x) {
+// Same sum with fp16 activations for MT tokens: x[t] holds token t's pairs
+// (x_2i, x_2i+1).  The nibbles are unpacked once for all tokens.
+template <int MT>
+__device__ __forceinline__ void dot_q4_0_f16(const u32x4 c, const cu32_p (&x)[MT], float (&out)[MT]) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float s_lo = 0.0f, s_hi = 0.0f;
+    float s_lo[MT], s_hi[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) s_lo[t] = s_hi[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const Q4Pairs p = q4_pairs(w[i]);
-        const uint32_t a = x[2 * i], b = x[2 * i + 1];          // x 4i .. 4i+3
-        const uint32_t ah = x[8 + 2 * i], bh = x[8 + 2 * i + 1]; // x 16+4i .. 16+4i+3
-        s_lo = __builtin_amdgcn_fdot2(p.t0, pack_ll(a, b), s_lo, false);
-        s_lo = __builtin_amdgcn_fdot2(p.t2, pack_hh(a, b), s_lo, false);
-        s_hi = __builtin_amdgcn_fdot2(p.t1, pack_ll(ah, bh), s_hi, false);
-        s_hi = __builtin_amdgcn_fdot2(p.t3, pack_hh(ah, bh), s_hi, false);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const uint32_t a = x[t][2 * i], b = x[t][2 * i + 1];          // x 4i .. 4i+3
+            const uint32_t ah = x[t][8 + 2 * i], bh = x[t][8 + 2 * i + 1]; // x 16+4i .. 16+4i+3
+            s_lo[t] = __builtin_amdgcn_fdot2(p.t0, pack_ll(a, b), s_lo[t], false);
+            s_lo[t] = __builtin_amdgcn_fdot2(p.t2, pack_hh(a, b), s_lo[t], false);
+            s_hi[t] = __builtin_amdgcn_fdot2(p.t1, pack_ll(ah, bh), s_hi[t], false);
+            s_hi[t] = __builtin_amdgcn_fdot2(p.t3, pack_hh(ah, bh), s_hi[t], false);
+        }
     }
-    return __builtin_fmaf(s_hi, 0.0625f, s_lo);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) out[t] = __builtin_fmaf(s_hi[t], 0.0625f, s_lo[t]);
 }
 
 // Signed byte n of a dword to fp32 in one VALU op (SDWA byte select with
@@ -170,22 +183,31 @@ __device__ __forceinline__ float dot_i8_f32(const u32x4 c0, const u32x4 c1, cf32
     return s0 + s1;
 }
 
-// Same with fp16 activations.  Flipping the sign bit of each byte gives
-// c + 128 in 0..255; a byte permute puts two of those under 0x64 (fp16
-// 1024 + v) and subtracting 1152 leaves the exact codes as an fp16 pair.
-__device__ __forceinline__ float dot_i8_f16(const u32x4 c0, const u32x4 c1, cu32_p x) {
+// Same with fp16 activations, MT tokens.  Flipping the sign bit of each
+// byte gives c + 128 in 0..255; a byte permute puts two of those under 0x64
+// (fp16 1024 + v) and subtracting 1152 leaves the exact codes as an fp16
+// pair, shared by all tokens.
+template <int MT>
+__device__ __forceinline__ void dot_i8_f16(const u32x4 c0, const u32x4 c1, const cu32_p (&x)[MT], int xoff,
+                                           float (&out)[MT]) {
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
-    float s0 = 0.0f, s1 = 0.0f;
+    float s0[MT], s1[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) s0[t] = s1[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t u = w[i] ^ 0x80808080u;
         const half2_t p01 = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off;
         const half2_t p23 = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
-        s0 = __builtin_amdgcn_fdot2(p01, as_half2(x[2 * i]), s0, false);
-        s1 = __builtin_amdgcn_fdot2(p23, as_half2(x[2 * i + 1]), s1, false);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            s0[t] = __builtin_amdgcn_fdot2(p01, as_half2(x[t][xoff + 2 * i]), s0[t], false);
+            s1[t] = __builtin_amdgcn_fdot2(p23, as_half2(x[t][xoff + 2 * i + 1]), s1[t], false);
+        }
     }
-    return s0 + s1;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) out[t] = s0[t] + s1[t];
 }
 
 template <int FMT>
@@ -195,29 +217,43 @@ struct Unit {
     uint32_t s;   // raw scale bits (fp16 in the low half, or fp32)
 };
 
-// scale * sum over unit u of code * x, added to acc.  keep is all ones, or
-// zero for a slot past the wave's last unit (its sum is dropped bit-wise, so
-// even an infinite or NaN sum adds nothing).
-template <int FMT, int XDT>
-__device__ __forceinline__ float unit_fma(const Unit<FMT>& b, const void* xv, int u, uint32_t keep,
-                                          float acc) {
+// scale * sum over unit u of code * x, added to acc[t] for each of the MT
+// tokens (token t's activations start xs 32-bit words after token 0's; MT > 1
+// only with fp16 activations).  keep is all ones, or zero for a slot past
+// the wave's last unit (its sum is dropped bit-wise, so even an infinite or
+// NaN sum adds nothing).
+template <int FMT, int XDT, int MT>
+__device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, size_t xs, int u, uint32_t keep,
+                                         float (&acc)[MT]) {
     constexpr int E = unit_elems(FMT);
-    float dot;
+    float dot[MT];
     if constexpr (XDT == kF32) {
+        static_assert(MT == 1, "several tokens take fp16 activations");
         const cf32_p x = (cf32_p)(xv) + size_t(u) * E;
-        if constexpr (FMT == kQ4_0) dot = dot_q4_0_f32(b.c[0], x);
-        else if constexpr (FMT == kQ8_0) dot = dot_i8_f32(b.c[0], b.c[1], x);
-        else dot = dot_i8_f32(b.c[0], b.c[1], x) + dot_i8_f32(b.c[2], b.c[3], x + 32);
+        if constexpr (FMT == kQ4_0) dot[0] = dot_q4_0_f32(b.c[0], x);
+        else if constexpr (FMT == kQ8_0) dot[0] = dot_i8_f32(b.c[0], b.c[1], x);
+        else dot[0] = dot_i8_f32(b.c[0], b.c[1], x) + dot_i8_f32(b.c[2], b.c[3], x + 32);
     } else {
-        const cu32_p x = (cu32_p)(xv) + size_t(u) * (E / 2);
-        if constexpr (FMT == kQ4_0) dot = dot_q4_0_f16(b.c[0], x);
-        else if constexpr (FMT == kQ8_0) dot = dot_i8_f16(b.c[0], b.c[1], x);
-        else dot = dot_i8_f16(b.c[0], b.c[1], x) + dot_i8_f16(b.c[2], b.c[3], x + 16);
+        cu32_p x[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) x[t] = (cu32_p)(xv) + size_t(t) * xs + size_t(u) * (E / 2);
+        if constexpr (FMT == kQ4_0) {
+            dot_q4_0_f16<MT>(b.c[0], x, dot);
+        } else if constexpr (FMT == kQ8_0) {
+            dot_i8_f16<MT>(b.c[0], b.c[1], x, 0, dot);
+        } else {
+            float d2[MT];
+            dot_i8_f16<MT>(b.c[0], b.c[1], x, 0, dot);
+            dot_i8_f16<MT>(b.c[2], b.c[3], x, 16, d2);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) dot[t] += d2[t];
+        }
     }
     float d;
     if constexpr (FMT == kI8B64) d = __uint_as_float(b.s);
     else d = (float)__builtin_bit_cast(_Float16, uint16_t(b.s));
-    return __builtin_fmaf(d, __uint_as_float(__float_as_uint(dot) & keep), acc);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = __builtin_fmaf(d, __uint_as_float(__float_as_uint(dot[t]) & keep), acc[t]);
 }
 
 // Largest batch of units one wave loads before computing them (register
@@ -247,12 +283,14 @@ __device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S)
 // launches whose matrices would otherwise split K across 4+ workgroups: the
 // split then stays inside the workgroup and needs no split-K round trips).
 // Each wave loads UNR units, then computes them, until its units are done.
-template <int FMT, int XDT, int W, int UNR>
+// MT tokens (1, or 2 with fp16 activations) share every weight load: x holds
+// MT rows of K values, y MT rows of N outputs.
+template <int FMT, int XDT, int W, int UNR, int MT>
 __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     constexpr int P = unit_parts(FMT);
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
-    __shared__ float red[W][kTileRows];
+    __shared__ float red[MT][W][kTileRows];
 
     // Matrix of this workgroup: the last descriptor whose first workgroup is
     // not after ours (uniform, scalar compares).
@@ -262,16 +300,22 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     const GemvDesc& D = a.d[di];
     const int N = D.N, nu = D.nu, S = D.S;
     const int local = bid - D.wg0;
-    const int tile = local / S;
-    const int slice = local - tile * S;
+    // Units [sa, sb) of this workgroup: slice `slice` of S.  (Unsplit
+    // matrices skip the divisions: with a few units per wave they are a
+    // noticeable share of the wave's scalar work.)
+    int tile = local, slice = 0, sa = 0, sb = nu;
+    if (S > 1) {
+        tile = local / S;
+        slice = local - tile * S;
+        sa = int(int64_t(nu) * slice / S);
+        sb = int(int64_t(nu) * (slice + 1) / S);
+    }
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int r = int(threadIdx.x) & 63;
     const int nr = min(kTileRows, N - tile * kTileRows);
     const int rc = min(r, nr - 1);   // lanes past the last row re-read it and store nothing
 
-    // Units [ua, ub) of this wave: slice `slice` of S, then quarter w of it.
-    const int sa = int(int64_t(nu) * slice / S);
-    const int sb = int(int64_t(nu) * (slice + 1) / S);
+    // Units [ua, ub) of this wave: part w of W of the slice.
     const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / W);
     const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / W);
 
@@ -286,8 +330,11 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     const uint32_t s_lane = uint32_t(rc) * SB;
     const uint32_t s_unit = uint32_t(nr) * SB;
     const void* x = D.x;
+    const size_t xs = size_t(nu) * (unit_elems(FMT) / 2);   // 32-bit words per fp16 token row
 
-    float acc = 0.0f;
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
     for (int u = ua; u < ub; u += UNR) {
         Unit<FMT> b[UNR];
 #pragma unroll
@@ -313,18 +360,27 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < UNR; ++k)
-            acc = unit_fma<FMT, XDT>(b[k], x, min(u + k, ub - 1), u + k < ub ? ~0u : 0u, acc);
+            unit_fma<FMT, XDT, MT>(b[k], x, xs, min(u + k, ub - 1), u + k < ub ? ~0u : 0u, acc);
     }
 
-    red[w][r] = acc;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[t][w][r] = acc[t];
     __syncthreads();
     if (w != 0) return;
-    float v = 0.0f;
+    float v[MT];
 #pragma unroll
-    for (int i = 0; i < W; i += 4) v += (red[i][r] + red[i + 1][r]) + (red[i + 2][r] + red[i + 3][r]);
+    for (int t = 0; t < MT; ++t) {
+        v[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < W; i += 4)
+            v[t] += (red[t][i][r] + red[t][i + 1][r]) + (red[t][i + 2][r] + red[t][i + 3][r]);
+    }
     const size_t row = size_t(tile) * kTileRows + size_t(r);
     if (S == 1) {
-        if (r < nr) D.y[row] = v;
+        if (r < nr) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) D.y[size_t(t) * N + row] = v[t];
+        }
         return;
     }
     // Split K: publish this slice, then the last arrival sums all slices.
@@ -337,24 +393,31 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     // times slower than the weight stream itself.  The store of the partials
     // must have completed (s_waitcnt 0) before the counter moves, and the
     // loads of the last arrival are issued only after its increment returned.
-    __hip_atomic_store(&D.part[size_t(slice) * pitch + row], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Slice j of token t sits at rows (j * MT + t) * pitch.
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        __hip_atomic_store(&D.part[(size_t(slice) * MT + t) * pitch + row], v[t], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     uint32_t prev = 0;
     if (r == 0)
         prev = __hip_atomic_fetch_add(&D.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev != uint32_t(S - 1)) return;
-    const float t = sum_slices(D.part + row, pitch, S);
-    if (r < nr) D.y[row] = t;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const float y = sum_slices(D.part + size_t(t) * pitch + row, MT * pitch, S);
+        if (r < nr) D.y[size_t(t) * N + row] = y;
+    }
     if (r == 0) __hip_atomic_store(&D.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int FMT, int XDT, int W, int UNR>
+template <int FMT, int XDT, int W, int UNR, int MT>
 hipError_t launch_unr(int unr, const GemvArgs& a, hipStream_t stream) {
     if constexpr (UNR > 1) {
-        if (unr < UNR) return launch_unr<FMT, XDT, W, UNR - 1>(unr, a, stream);
+        if (unr < UNR) return launch_unr<FMT, XDT, W, UNR - 1, MT>(unr, a, stream);
     }
-    hipLaunchKernelGGL((gemv_kernel<FMT, XDT, W, UNR>), dim3(unsigned(a.total_wgs)), dim3(64u * W), 0,
+    hipLaunchKernelGGL((gemv_kernel<FMT, XDT, W, UNR, MT>), dim3(unsigned(a.total_wgs)), dim3(64u * W), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -378,16 +441,31 @@ int launch_unroll(int fmt, int waves, const GemvArgs& a) {
     return (u + batches - 1) / batches;
 }
 
+template <int FMT, int MT>
+hipError_t launch_tokens(int waves, int mt, int unr, const GemvArgs& a, hipStream_t stream) {
+    if constexpr (MT > 2) {
+        if (mt < MT) return launch_tokens<FMT, MT - 1>(waves, mt, unr, a, stream);
+    }
+    constexpr int CAP = unroll_cap(FMT) > 2 ? unroll_cap(FMT) : 2;
+    if (waves == 16) return launch_unr<FMT, kF16, 16, CAP, MT>(unr, a, stream);
+    return launch_unr<FMT, kF16, 4, CAP, MT>(unr, a, stream);
+}
+
 template <int FMT>
-hipError_t launch_fmt(int xdt, int waves, const GemvArgs& a, hipStream_t stream) {
+hipError_t launch_fmt(int xdt, int waves, int mt, const GemvArgs& a, hipStream_t stream) {
     constexpr int CAP = unroll_cap(FMT) > 2 ? unroll_cap(FMT) : 2;
     const int unr = launch_unroll(FMT, waves, a);
-    if (waves == 16) {
-        if (xdt == kF32) return launch_unr<FMT, kF32, 16, CAP>(unr, a, stream);
-        return launch_unr<FMT, kF16, 16, CAP>(unr, a, stream);
+    if (mt > 1) {
+        if (xdt != kF16 || mt > gemv_max_tokens(FMT)) return hipErrorInvalidValue;
+        return launch_tokens<FMT, gemv_max_tokens(FMT)>(waves, mt, unr, a, stream);
     }
-    if (xdt == kF32) return launch_unr<FMT, kF32, 4, CAP>(unr, a, stream);
-    return launch_unr<FMT, kF16, 4, CAP>(unr, a, stream);
+    if (mt != 1) return hipErrorInvalidValue;
+    if (waves == 16) {
+        if (xdt == kF32) return launch_unr<FMT, kF32, 16, CAP, 1>(unr, a, stream);
+        return launch_unr<FMT, kF16, 16, CAP, 1>(unr, a, stream);
+    }
+    if (xdt == kF32) return launch_unr<FMT, kF32, 4, CAP, 1>(unr, a, stream);
+    return launch_unr<FMT, kF16, 4, CAP, 1>(unr, a, stream);
 }
 
 std::mutex g_scratch_mu;
@@ -417,12 +495,12 @@ hipError_t gemv_scratch(float** part, uint32_t** cnt) {
     return hipSuccess;
 }
 
-hipError_t launch_gemv(int fmt, int xdt, int waves, const GemvArgs& a, hipStream_t stream) {
+hipError_t launch_gemv(int fmt, int xdt, int waves, int mt, const GemvArgs& a, hipStream_t stream) {
     if (waves != 4 && waves != 16) return hipErrorInvalidValue;
     switch (fmt) {
-        case kQ4_0: return launch_fmt<kQ4_0>(xdt, waves, a, stream);
-        case kQ8_0: return launch_fmt<kQ8_0>(xdt, waves, a, stream);
-        case kI8B64: return launch_fmt<kI8B64>(xdt, waves, a, stream);
+        case kQ4_0: return launch_fmt<kQ4_0>(xdt, waves, mt, a, stream);
+        case kQ8_0: return launch_fmt<kQ8_0>(xdt, waves, mt, a, stream);
+        case kI8B64: return launch_fmt<kI8B64>(xdt, waves, mt, a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -108,9 +108,9 @@ inline int multi_min_units(int fmt) { return fmt == kI8B64 ? 2 : 8; }
 struct GemvDesc {
     const uint8_t* codes;   // code plane (tiled)
     const uint8_t* scales;  // scale plane (tiled)
-    const void* x;          // activations (fp32 or fp16), K values
-    float* y;               // N outputs
-    float* part;            // split-K partials: S slices x tiles * 64 floats (S > 1 only)
+    const void* x;          // activations (fp32 or fp16): MT rows of K values
+    float* y;               // MT rows of N outputs
+    float* part;            // split-K partials: S slices x MT tokens x tiles * 64 floats (S > 1 only)
     uint32_t* cnt;          // one arrival counter per tile (S > 1 only)
     int32_t N;              // rows
     int32_t nu;             // units per row (K / unit_elems)
@@ -126,7 +126,14 @@ struct GemvArgs {
     int32_t total_wgs;
 };
 
-hipError_t launch_gemv(int fmt, int xdt, int waves, const GemvArgs& args, hipStream_t stream);
+// Most tokens one GEMV launch takes (MT > 1 only with fp16 activations).
+// Every weight is decoded once for all tokens, and each token adds one fp16
+// dot product per weight pair: Q4_0 (the costliest decode per byte) stays
+// under the weight stream's time up to two tokens, Q8_0 and int8 block-64
+// up to four.
+__host__ __device__ constexpr int gemv_max_tokens(int fmt) { return fmt == kQ4_0 ? 2 : 4; }
+// mt: tokens of the launch, 1 .. gemv_max_tokens(fmt).
+hipError_t launch_gemv(int fmt, int xdt, int waves, int mt, const GemvArgs& args, hipStream_t stream);
 // Device addresses of this device's split-K scratch (looked up once per device).
 hipError_t gemv_scratch(float** part, uint32_t** cnt);
 

@@ -4,7 +4,10 @@ Y[m, n] = sum_k w[n,k] X[m,k] for up to 16 tokens with fp16 activations.  The
 bar is the single-token GEMV's, per output: |Y - Y_ref| <= 1e-4 * sum|w x| +
 1e-6, since the weights are decoded exactly and only the fp32 sums round.
 Shapes span several 64-row tiles, partial last tiles, one-block rows, K split
-across workgroups, and every token count from 1 to 16.
+across workgroups, and every token count from 1 to 16.  Up to two tokens
+(Q4_0) or four (Q8_0, int8 block-64) run on the single-token GEMV kernel
+(each token row then equals lq_gemv of that row bit for bit); more on the
+matrix-core kernel.
 """
 import sys
 
@@ -46,6 +49,11 @@ MULTI_SHAPES = [
     ("q8_0", 11, 200, 5632), ("q8_0", 16, 1100, 1024),
     ("i8b64", 1, 1, 64), ("i8b64", 3, 77, 128), ("i8b64", 16, 256, 2048), ("i8b64", 6, 45, 5632),
     ("i8b64", 16, 130, 8192), ("i8b64", 9, 5, 30720), ("i8b64", 14, 1500, 512),
+    # GEMV-kernel token counts: K split across workgroups, 16-wave workgroups, ragged tiles
+    ("q4_0", 2, 17, 25600), ("q4_0", 2, 2500, 896), ("q4_0", 1, 200, 4096),
+    ("q8_0", 2, 130, 8192), ("q8_0", 1, 200, 5632), ("q8_0", 3, 3000, 2048), ("q8_0", 4, 77, 4096),
+    ("q8_0", 4, 8200, 1024),
+    ("i8b64", 2, 45, 5632), ("i8b64", 1, 130, 8192), ("i8b64", 3, 1500, 512), ("i8b64", 4, 300, 8192),
 ]
 
 
@@ -63,12 +71,13 @@ def test_multi_parity(oracle, fmt, M, N, K):
     assert r <= 1.0, f"tolerance ratio {r}"
 
 
+@pytest.mark.parametrize("M", [16, 4, 2])
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
-def test_multi_invariants(oracle, fmt):
+def test_multi_invariants(oracle, fmt, M):
     """Deterministic; doubling every scale doubles Y bit for bit; a one-hot
     token row gives the weight column exactly as lq_dequant_f32 unpacks it;
     each token row agrees with the single-token GEMV of that row."""
-    M, N, K = 16, 200, 2048 if fmt != "q4_0" else 896
+    N, K = 200, 2048 if fmt != "q4_0" else 896
     say("gemv_multi invariants", fmt, M, N, K)
     w, s = make(fmt, 4321, N, K)
     X = lqgen.activations(77, M * K, np.float16).reshape(M, K)
@@ -91,16 +100,34 @@ def test_multi_invariants(oracle, fmt):
     torch.cuda.synchronize()
     full = out32.cpu().numpy().reshape(N, K)
     ks = [0, 1, 15, 16, 31, 32, 63, 100, 257, 511, 640, K - 33, K - 17, K - 2, K - 1, 5]
-    E = np.zeros((M, K), np.float16)
-    for m, k in enumerate(ks):
-        E[m, k] = 1
-    Ye = gu.gemv_multi(fmt, Wd, E, M, N, K)
-    for m, k in enumerate(ks):
-        assert np.array_equal(Ye[m].view(np.uint32), full[:, k].view(np.uint32)), (m, k)
-    for m in (0, 7, 15):
+    for j in range(0, len(ks), M):
+        E = np.zeros((M, K), np.float16)
+        for m, k in enumerate(ks[j:j + M]):
+            E[m, k] = 1
+        Ye = gu.gemv_multi(fmt, Wd, E, M, N, K)
+        for m, k in enumerate(ks[j:j + M]):
+            assert np.array_equal(Ye[m].view(np.uint32), full[:, k].view(np.uint32)), (m, k)
+    for m in sorted({0, M // 2, M - 1}):
         y = gu.gemv(fmt, Wd, X[m], N, K)
         _, S = oracle.gemv(ORACLE_FMT[fmt], w, s, X[m], N, K)
         assert np.all(np.abs(Y1[m].astype(np.float64) - y) <= 2 * (gu.GEMV_REL * S + gu.GEMV_ABS)), m
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 2, 151936 // 8, 896), ("q4_0", 2, 70, 25600),
+                                        ("q8_0", 2, 8192, 2048), ("q8_0", 3, 130, 8192), ("q8_0", 4, 2048, 8192),
+                                        ("i8b64", 2, 300, 5632), ("i8b64", 3, 2048, 8192), ("i8b64", 4, 70, 8192)])
+def test_few_tokens_equal_single_token_rows(fmt, M, N, K):
+    """A few tokens share each weight load, but every token row goes through
+    the arithmetic of lq_gemv with fp16 activations on the same K split: the
+    rows are those GEMVs bit for bit (split and unsplit K)."""
+    say("gemv_multi few tokens vs lq_gemv", fmt, M, N, K)
+    w, s = make(fmt, 3300 + N + K, N, K)
+    Wd = gu.upload(fmt, w, s, N, K)
+    X = lqgen.activations(3400 + K + M, M * K, np.float16).reshape(M, K)
+    Y = gu.gemv_multi(fmt, Wd, X, M, N, K)
+    for m in range(M):
+        y = gu.gemv(fmt, Wd, X[m], N, K)
+        assert np.array_equal(Y[m].view(np.uint32), y.view(np.uint32)), m
 
 
 def test_multi_zero_codes():
