@@ -200,9 +200,9 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
  *   Y[m, n] = sum_k w[n,k] * X[m,k]   for m < M, n < N,
  * every weight read once for all M tokens.  The weights are decoded exactly
  * (fp16 x exact integer code, fp32 block sums), the block scale applied in
- * fp32: for M <= 2 as lq_gemv does it, each token row then being lq_gemv of
- * that row (fp16 x) bit for bit; for M >= 3 on the matrix cores.  W: packed
- * N x K; X: M x K fp16
+ * fp32: for M <= 2 (LQ_Q4_0) or M <= 4 (LQ_Q8_0, LQ_I8B64) as lq_gemv does
+ * it, each token row then being lq_gemv of that row (fp16 x) bit for bit;
+ * for more tokens on the matrix cores.  W: packed N x K; X: M x K fp16
  * row-major (xdt must be LQ_F16, else LQ_ERR_UNSUPPORTED); Y: M x N fp32
  * row-major.  1 <= M <= 16, else LQ_ERR_SHAPE.  Accuracy as lq_gemv, per
  * output: |Y - Y_exact| <= 1e-4 * sum_k |w x| + 1e-6.  Shares the GEMV
@@ -228,7 +228,8 @@ typedef struct lq_gemv_multi_desc {
  * small matrices share launches.  descs: HOST array of `count` descriptors
  * (count >= 1), read during the call only; all are validated before anything
  * is enqueued.  Descriptors of one format run in one kernel launch (up to 16
- * per launch), except that M = 1, M = 2 and M >= 3 take separate launches. */
+ * per launch), except that each M run on the lq_gemv kernel (see
+ * lq_gemv_multi) takes a launch of its own. */
 lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* stream);
 
 /* Workspace bytes lq_gemm needs for these arguments (0 means none). */
