@@ -30,7 +30,8 @@
 //     workspace and a second kernel adds the slices in order (deterministic).
 //   * Workgroups that read the same weights (same N tile, different M tile)
 //     are placed on the same XCD so the second read hits that XCD's L2.
-//   * The epilogue stages the tile through LDS so stores are whole rows.
+//   * The epilogue stores straight from the accumulators (128-byte row
+//     segments).
 #include "lq_internal.h"
 
 #include <algorithm>
@@ -73,9 +74,7 @@ struct Cfg {
     static constexpr int kBTileBytes = BN * 64;
     static constexpr int kBOff = kStages * kSlotBytes;
     static constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;     // <= 159,744
-    static constexpr int kCPitch = BN + 8;                        // epilogue row pitch (floats)
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
-    static_assert(128 * kCPitch * 4 <= kLdsBytes, "epilogue staging");
     static_assert(kStages >= 5, "the unpack needs step st + 2 landed");
 };
 
@@ -354,46 +353,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[s][i], b0[s][j], acc[i][j], 0, 0, 0);
     }
 
-    // ---- epilogue: the tile goes through LDS in two halves of 128 rows so
-    // global stores are whole rows, 16 bytes per lane.  32x32 accumulator
+    // ---- epilogue: straight from the accumulators.  32x32 accumulator
     // layout: register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
-    // column l % 32.  Row pitch BN + 8 floats: the two half waves (rows 4
-    // apart) write disjoint banks.
-    constexpr int kCPitch = C::kCPitch;
-    constexpr int kChunks = BN / 4;                  // 16-byte chunks per row
-    float* cst = reinterpret_cast<float*>(lds);
+    // column l % 32, so each store writes two 128-byte row segments.  (Staging
+    // the tile through LDS for whole-row 16-byte stores took two barriers and
+    // was 1.4 us slower on the 2048 x 11008 gate + up launch at M = 512.)
     float* out = G.out + size_t(ks) * size_t(a.M) * size_t(G.N);
     const int n0 = tn * BN;
-    const bool full = m0 + BM <= a.M && n0 + BN <= G.N && (G.N & 3) == 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        __syncthreads();
-        if ((wm >> 1) == half) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < NT; ++j) {
+            const int col = n0 + wn * 32 * NT + j * 32 + (lane & 31);
 #pragma unroll
-                for (int j = 0; j < NT; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = (wm & 1) * 64 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                        cst[row * kCPitch + wn * 32 * NT + j * 32 + (lane & 31)] = acc[i][j][r];
-                    }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < 128 * kChunks; idx += kThreads) {
-            const int row = idx / kChunks;
-            const int col = (idx - row * kChunks) * 4;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(cst + row * kCPitch + col);
-            const int m = m0 + half * 128 + row;
-            if (full) {
-                *reinterpret_cast<f32x4*>(out + size_t(m) * size_t(G.N) + n0 + col) = v;
-            } else if (m < a.M) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n0 + col + e < G.N) out[size_t(m) * size_t(G.N) + n0 + col + e] = v[e];
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                if (row < a.M && col < G.N) out[size_t(row) * size_t(G.N) + col] = acc[i][j][r];
             }
         }
-    }
 }
 
 // Y = sum of the S partial slices, added in slice order.
