@@ -159,6 +159,46 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
         tiles[i] = (g[i].N + lq::kTileRows - 1) / lq::kTileRows;
         nu[i] = g[i].K / lq::unit_elems(fmt);
     }
+    // Few tiles of a multi-part format (even split by rows into
+    // unit_parts(fmt) workgroups each, no more workgroups than CUs), short
+    // rows: split each tile by rows instead of K (no split-K round trips;
+    // see launch_gemv_sub).  Measured on the int8 block-64 decoder layer:
+    // q/k/v 5.0 -> 3.8 us, o 4.7 -> 3.6, down 7.0 -> 6.2; gate/up (176 tiles,
+    // 704 sub-tile workgroups) was slower, 6.2 -> 7.7, and keeps the K split.
+    // The choice does not depend on mt, so each token row of a few-token
+    // launch is the one-token result bit for bit.
+    int64_t total_tiles = 0, max_nu = 0;
+    for (int i = 0; i < n; ++i) {
+        total_tiles += tiles[i];
+        max_nu = std::max(max_nu, nu[i]);
+    }
+    if (fmt != LQ_Q4_0 && total_tiles * lq::unit_parts(fmt) <= cus && max_nu <= LQ_GEMV_SUB_MAX_UNITS) {
+        const int parts = lq::unit_parts(fmt);
+        lq::GemvArgs a = {};
+        int64_t wgs = 0;
+        for (int i = 0; i < n; ++i) {
+            const GemvJob& d = g[i];
+            lq::GemvDesc& o = a.d[i];
+            o.codes = static_cast<const uint8_t*>(d.W);
+            o.scales = static_cast<const uint8_t*>(d.W) + lq::align256(lq::code_plane_bytes(fmt, d.N, d.K));
+            o.x = d.x;
+            o.y = d.y;
+            o.N = int32_t(d.N);
+            o.nu = int32_t(nu[i]);
+            o.tiles = int32_t(tiles[i]);
+            o.S = 1;
+            o.wg0 = int32_t(wgs);
+            o.pad = 0;
+            o.part = nullptr;
+            o.cnt = nullptr;
+            wgs += tiles[i] * parts;
+        }
+        a.count = n;
+        a.total_wgs = int32_t(wgs);
+        const hipError_t e = lq::launch_gemv_sub(fmt, xdt, mt, a, stream);
+        if (e != hipSuccess) return hip_fail(e, "GEMV launch");
+        return LQ_OK;
+    }
     split_k(lq::gemv_min_units(fmt), cus, tiles, nu, std::vector<int64_t>(n, mt), S);
     // When every matrix splits K at least LQ_GEMV_WIDE_FROM ways, the launch
     // uses 16-wave workgroups: four of the K slices move inside a workgroup

@@ -41,6 +41,7 @@
 #include "lq_internal.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace lq {
 
@@ -55,6 +56,7 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Activations are read through the constant address space so that uniform
 // indices turn into scalar loads.
 typedef const __attribute__((address_space(4))) float* cf32_p;
@@ -412,6 +414,156 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     if (r == 0) __hip_atomic_store(&D.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16 weights (one code part) times 16 activations held in VGPRs: the sub-tile
+// kernel's lanes each take one part of a unit, so their activations differ
+// between lane groups and cannot sit in SGPRs.
+__device__ __forceinline__ float dot16_i8(const u32x4 c, const u32x4 (&x)[2]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t xx[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = w[i] ^ 0x80808080u;
+        const half2_t p01 = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off;
+        const half2_t p23 = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
+        s0 = __builtin_amdgcn_fdot2(p01, as_half2(xx[2 * i]), s0, false);
+        s1 = __builtin_amdgcn_fdot2(p23, as_half2(xx[2 * i + 1]), s1, false);
+    }
+    return s0 + s1;
+}
+__device__ __forceinline__ float dot16_i8(const u32x4 c, const f32x4 (&x)[4]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d = w[i];
+        s0 = __builtin_fmaf(sbyte0(d), x[i].x, s0);
+        s1 = __builtin_fmaf(sbyte1(d), x[i].y, s1);
+        s0 = __builtin_fmaf(sbyte2(d), x[i].z, s0);
+        s1 = __builtin_fmaf(sbyte3(d), x[i].w, s1);
+    }
+    return s0 + s1;
+}
+
+// Sub-tile GEMV (Q8_0 and int8 block-64) for launches of few 64-row tiles
+// (at most one workgroup per CU after the split below), e.g. one decoder
+// layer's q/k/v or o projection alone: each tile is split across P workgroups by rows instead of across
+// workgroups by K, so P times as many CUs stream it and no partial sum
+// leaves its workgroup.  Workgroup (tile, sub) owns rows sub * RPW .. + RPW
+// of the tile (RPW = 64 / P, P = 2 or 4 code parts per unit); lane l takes
+// row l % RPW and part l / RPW (16 weights) of each unit, so a wave's load is
+// still P whole pieces of the unit's contiguous runs.  The 16 waves split
+// the units; the part and wave sums of a row are added in LDS in a fixed
+// order.  MT tokens (fp16 activations when MT > 1) share the weight loads;
+// each token's arithmetic is the same as with MT = 1, and a slot past a
+// wave's last unit leaves the sums untouched, so the batch size never
+// changes a result.
+template <int FMT, int XDT, int UNR, int MT>
+__global__ __launch_bounds__(1024) void gemv_sub_kernel(const GemvArgs a) {
+    constexpr int W = 16;
+    constexpr int P = unit_parts(FMT);
+    static_assert(P > 1, "rows are split by code part");
+    static_assert(MT == 1 || XDT == kF16, "several tokens take fp16 activations");
+    constexpr int RPW = kTileRows / P;
+    constexpr int E = unit_elems(FMT);
+    constexpr int UB = unit_bytes(FMT);
+    constexpr int SB = scale_bytes(FMT);
+    __shared__ float red[MT][W][kTileRows];
+
+    const int bid = blockIdx.x;
+    int di = 0;
+    for (int i = 1; i < a.count; ++i) di += bid >= a.d[i].wg0 ? 1 : 0;
+    const GemvDesc& D = a.d[di];
+    const int N = D.N, nu = D.nu;
+    const int local = bid - D.wg0;
+    const int tile = local / P;
+    const int sub = local - tile * P;
+    const int nr = min(kTileRows, N - tile * kTileRows);
+    if (sub * RPW >= nr) return;   // whole workgroup: past the last row of a ragged tile
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int l = int(threadIdx.x) & 63;
+    const int p = l / RPW;
+    const int rr = sub * RPW + (l - p * RPW);   // row within the tile
+    const int rc = min(rr, nr - 1);              // rows past the last re-read it and store nothing
+    const int ua = __builtin_amdgcn_readfirstlane(nu * w / W);
+    const int ub = __builtin_amdgcn_readfirstlane(nu * (w + 1) / W);
+
+    const size_t first = size_t(tile) * kTileRows * size_t(nu);
+    const uint8_t* cbase = D.codes + first * UB;
+    const uint8_t* sbase = D.scales + first * SB;
+    const uint32_t c_lane = uint32_t(p) * uint32_t(nr) * 16u + uint32_t(rc) * 16u;
+    const uint32_t c_unit = uint32_t(nr) * UB;
+    const uint32_t s_lane = uint32_t(rc) * SB;
+    const uint32_t s_unit = uint32_t(nr) * SB;
+    constexpr int XB = XDT == kF32 ? 4 : 2;    // bytes per activation
+    constexpr int XV = XB;                     // 16-byte loads per 16 activations
+    using XT = typename std::conditional<XDT == kF32, f32x4, u32x4>::type;
+    const size_t xrow = size_t(nu) * E * XB / 16;   // one token's activations, in 16-byte units
+    const XT* xb = reinterpret_cast<const XT*>(static_cast<const uint8_t*>(D.x) + size_t(p) * 16 * XB);
+
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+    for (int u = ua; u < ub; u += UNR) {
+        u32x4 c[UNR];
+        uint32_t sc[UNR];
+        XT x[UNR][MT][XV];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t uu = uint32_t(min(u + k, ub - 1));
+            c[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + uu * c_unit + c_lane));
+            const uint32_t so = uu * s_unit + s_lane;
+            if constexpr (SB == 2)
+                sc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + so));
+            else
+                sc[k] = *reinterpret_cast<const uint32_t*>(sbase + so);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int v = 0; v < XV; ++v) x[k][t][v] = xb[size_t(t) * xrow + size_t(uu) * (E / 16) * XV + v];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            float d;
+            if constexpr (SB == 4) d = __uint_as_float(sc[k]);
+            else d = (float)__builtin_bit_cast(_Float16, uint16_t(sc[k]));
+            const bool keep = u + k < ub;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const float f = __builtin_fmaf(d, dot16_i8(c[k], x[k][t]), acc[t]);
+                acc[t] = keep ? f : acc[t];
+            }
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[t][w][l] = acc[t];
+    __syncthreads();
+    if (w != 0 || l >= RPW) return;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+#pragma unroll
+            for (int i = 0; i < W; i += 4)
+                v += (red[t][i][q * RPW + l] + red[t][i + 1][q * RPW + l]) +
+                     (red[t][i + 2][q * RPW + l] + red[t][i + 3][q * RPW + l]);
+        if (rr < nr) D.y[size_t(t) * N + size_t(tile) * kTileRows + size_t(rr)] = v;
+    }
+}
+
+template <int FMT, int XDT, int UNR, int MT>
+hipError_t launch_sub_unr(int unr, const GemvArgs& a, hipStream_t stream) {
+    if constexpr (UNR > 1) {
+        if (unr < UNR) return launch_sub_unr<FMT, XDT, UNR - 1, MT>(unr, a, stream);
+    }
+    hipLaunchKernelGGL((gemv_sub_kernel<FMT, XDT, UNR, MT>), dim3(unsigned(a.total_wgs)), dim3(1024u), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int FMT, int XDT, int W, int UNR, int MT>
 hipError_t launch_unr(int unr, const GemvArgs& a, hipStream_t stream) {
     if constexpr (UNR > 1) {
@@ -468,6 +620,25 @@ hipError_t launch_fmt(int xdt, int waves, int mt, const GemvArgs& a, hipStream_t
     return launch_unr<FMT, kF16, 4, CAP, 1>(unr, a, stream);
 }
 
+// Units a sub-tile wave loads before computing them: a launch's waves have
+// at most u = ceil(nu / 16) units, run in equal batches of at most 4 (one
+// token) or 2 (several: their activations take the registers).
+template <int FMT, int MT>
+hipError_t launch_sub_tokens(int xdt, int mt, const GemvArgs& a, hipStream_t stream) {
+    if constexpr (MT > 1) {
+        if (mt < MT) return launch_sub_tokens<FMT, MT - 1>(xdt, mt, a, stream);
+    }
+    constexpr int CAP = MT == 1 ? 4 : 2;
+    int u = 1;
+    for (int i = 0; i < a.count; ++i) u = max(u, (a.d[i].nu + 15) / 16);
+    const int batches = (u + CAP - 1) / CAP;
+    const int unr = (u + batches - 1) / batches;
+    if constexpr (MT == 1) {
+        if (xdt == kF32) return launch_sub_unr<FMT, kF32, CAP, 1>(unr, a, stream);
+    }
+    return launch_sub_unr<FMT, kF16, CAP, MT>(unr, a, stream);
+}
+
 std::mutex g_scratch_mu;
 float* g_part_addr[64] = {nullptr};
 uint32_t* g_cnt_addr[64] = {nullptr};
@@ -493,6 +664,15 @@ hipError_t gemv_scratch(float** part, uint32_t** cnt) {
     *part = g_part_addr[dev];
     *cnt = g_cnt_addr[dev];
     return hipSuccess;
+}
+
+hipError_t launch_gemv_sub(int fmt, int xdt, int mt, const GemvArgs& a, hipStream_t stream) {
+    if (mt < 1 || mt > gemv_max_tokens(fmt) || (mt > 1 && xdt != kF16)) return hipErrorInvalidValue;
+    switch (fmt) {
+        case kQ8_0: return launch_sub_tokens<kQ8_0, gemv_max_tokens(kQ8_0)>(xdt, mt, a, stream);
+        case kI8B64: return launch_sub_tokens<kI8B64, gemv_max_tokens(kI8B64)>(xdt, mt, a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemv(int fmt, int xdt, int waves, int mt, const GemvArgs& a, hipStream_t stream) {

@@ -98,6 +98,14 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #ifndef LQ_GEMV_MIN_UNITS_I8
 #define LQ_GEMV_MIN_UNITS_I8 2
 #endif
+// Launches of formats with several code parts per unit whose tiles, split
+// by rows into unit_parts(fmt) workgroups each, are no more than the
+// device's CUs split tiles that way (launch_gemv_sub), for any token count,
+// when no matrix has more than this many units per row (16 waves then get at most 8
+// units each); longer rows keep the K split across workgroups.
+#ifndef LQ_GEMV_SUB_MAX_UNITS
+#define LQ_GEMV_SUB_MAX_UNITS 128
+#endif
 inline int gemv_min_units(int fmt) {
     return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kQ8_0 ? LQ_GEMV_MIN_UNITS_Q8 : LQ_GEMV_MIN_UNITS_I8);
 }
@@ -134,6 +142,11 @@ struct GemvArgs {
 __host__ __device__ constexpr int gemv_max_tokens(int fmt) { return fmt == kQ4_0 ? 2 : 4; }
 // mt: tokens of the launch, 1 .. gemv_max_tokens(fmt).
 hipError_t launch_gemv(int fmt, int xdt, int waves, int mt, const GemvArgs& args, hipStream_t stream);
+// Q8_0 / int8 block-64, mt tokens (as launch_gemv), K unsplit: each 64-row
+// tile is split by rows across unit_parts(fmt) workgroups of 16 waves
+// (args.total_wgs counts those workgroups, d[i].wg0 the first of matrix i,
+// d[i].S must be 1).
+hipError_t launch_gemv_sub(int fmt, int xdt, int mt, const GemvArgs& args, hipStream_t stream);
 // Device addresses of this device's split-K scratch (looked up once per device).
 hipError_t gemv_scratch(float** part, uint32_t** cnt);
 
