@@ -267,3 +267,43 @@ def test_workload_multi_q8_0_layer(oracle):
 @pytest.mark.slow
 def test_workload_multi_i8b64_layer(oracle):
     _workload(oracle, lqgen.multi_token(lqgen.i8b64_tinyllama_layer(0), 4), 1024)
+
+
+def _grouped_workload(oracle, wl, sample):
+    """Every matrix of the workload in one lq_gemv_multi_batch call (the
+    launch bench.py times), sampled rows of each against the oracle."""
+    M = wl.M
+    mats = [(m,) + tuple(m.generate()) for m in wl.mats]
+    X = {k: wl.x(k) for k in wl.xs}
+    Xd = {k: to_device(v) for k, v in X.items()}
+    descs, outs, devs = [], [], []
+    for m, w, s in mats:
+        Wd, Y = gu.upload(m.fmt, w, s, m.N, m.K), gu.guarded(M * m.N)
+        devs.append(Wd)
+        descs.append((gu.FMT[m.fmt], Wd, Xd[m.xkey], Y, M, m.N, m.K))
+        outs.append(Y)
+    say("gemv_multi grouped workload", wl.name, M, len(mats))
+    lq.lq_gemv_multi_batch(descs)
+    torch.cuda.synchronize()
+    for (m, w, s), Y in zip(mats, outs):
+        gu.check_guard(Y, M * m.N)
+        got = Y[:M * m.N].cpu().numpy().reshape(M, m.N)
+        rng = np.random.default_rng(m.seed + M)
+        ns = np.unique(np.concatenate([[0, 1, 63, 64, m.N - 2, m.N - 1], rng.integers(0, m.N, sample)]))
+        Yr, S = oracle.gemm(ORACLE_FMT[m.fmt], w, s, X[m.xkey], M, m.N, m.K, ns=ns)
+        assert gu.ratio(got[:, ns], Yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0, (wl.name, m.name, M)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [2, 4])
+def test_workload_few_tokens_q8_0_layer_grouped(oracle, M):
+    """The Q8_0 decoder layer at M = 2 and 4 in one grouped launch, as timed
+    (few-token GEMV kernel, K split on the down projection)."""
+    _grouped_workload(oracle, lqgen.multi_token(lqgen.q8_0_layer_2048(0), M), 1024)
+
+
+@pytest.mark.slow
+def test_workload_few_tokens_lm_head(oracle):
+    """The Q4_0 LM head at M = 2 (few-token GEMV kernel), as timed."""
+    wl = lqgen.multi_token(lqgen.q4_0_lmhead_151936x896(with_ffn=False), 2)
+    _grouped_workload(oracle, wl, 4096)
