@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblq.so")
-SOURCES = ["lq_api.hip", "lq_gemv.hip", "lq_multi.hip", "lq_convert.hip", "lq_gemm.hip", "lq_prefill.hip"]
+SOURCES = ["lq_api.hip", "lq_gemv.hip", "lq_multi.hip", "lq_convert.hip", "lq_gemm.hip"]
 ARCH = os.environ.get("LQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,12 +27,10 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-command-line-argument"]
 
 
-# Per-source extra flags.  The multi-token GEMV and the register-fragment
-# prefill GEMM take their MFMA results in ordinary VGPRs (the compiler
-# otherwise routes them through accumulation registers and copies each one
-# back).
-EXTRA = {"lq_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "lq_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The multi-token GEMV takes its MFMA results in
+# ordinary VGPRs (the compiler otherwise routes them through accumulation
+# registers and copies each one back).
+EXTRA = {"lq_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -505,13 +505,7 @@ lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, 
 }
 
 namespace {
-// Q4_0 and Q8_0: the LDS-tile GEMM (fp16 weight tiles); int8 block-64 (fp32
-// scales, not an fp16 tile): the register-fragment one.
-bool use_lds_tile_gemm(int32_t fmt) { return fmt == LQ_Q4_0 || fmt == LQ_Q8_0; }
-
-size_t gemm_ws(int32_t fmt, int64_t M, int64_t N, int64_t K) {
-    return use_lds_tile_gemm(fmt) ? lq::gemm_workspace_bytes(M, N, K) : lq::prefill_workspace_bytes(M, N, K);
-}
+size_t gemm_ws(int32_t fmt, int64_t M, int64_t N, int64_t K) { return lq::gemm_workspace_bytes(fmt, M, N, K); }
 }  // namespace
 
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
@@ -545,30 +539,23 @@ lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int6
         LQ_TRY(check_ptr(descs[i].Y, 4, "Y"));
         need = std::max(need, gemm_ws(fmt, M, descs[i].N, K));
     }
-    if (use_lds_tile_gemm(fmt) && count > 1) need = 0;   // one launch, K not split
+    if (count > 1) need = 0;   // one launch, K not split
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, ws_bytes);
     if (ws && !aligned(ws, 16)) return fail(LQ_ERR_ALIGN, "ws is not 16-byte aligned");
     int cus = 0;
     LQ_TRY(device_cus(&cus));
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (use_lds_tile_gemm(fmt)) {
-        const void* W[lq::kMaxGemmGroup];
-        float* Y[lq::kMaxGemmGroup];
-        int64_t N[lq::kMaxGemmGroup];
-        for (int i = 0; i < count; ++i) {
-            W[i] = descs[i].W;
-            Y[i] = descs[i].Y;
-            N[i] = descs[i].N;
-        }
-        const hipError_t e = lq::launch_gemm_tile(fmt, W, Y, N, count, X, M, K, ws, cus, s);
-        return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
-    }
+    const void* W[lq::kMaxGemmGroup];
+    float* Y[lq::kMaxGemmGroup];
+    int64_t N[lq::kMaxGemmGroup];
     for (int i = 0; i < count; ++i) {
-        const hipError_t e = lq::launch_prefill(fmt, descs[i].W, X, descs[i].Y, M, descs[i].N, K, ws, s);
-        if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+        W[i] = descs[i].W;
+        Y[i] = descs[i].Y;
+        N[i] = descs[i].N;
     }
-    return LQ_OK;
+    const hipError_t e = lq::launch_gemm_tile(fmt, W, Y, N, count, X, M, K, ws, cus, s);
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "GEMM launch");
 }
 
 lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,

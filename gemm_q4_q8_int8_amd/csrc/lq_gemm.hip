@@ -1,11 +1,15 @@
-// Prefill GEMM for Q4_0 weights: Y[M x N] = X[M x K] * W[N x K]^T.
+// Prefill GEMM for Q4_0, Q8_0 and int8 block-64 weights:
+// Y[M x N] = X[M x K] * W[N x K]^T.
 //
 // Prefill is compute-bound ("oxinfer" page, "Performance"), and the GPU
 // kernels the page describes dequantize the weight tile on chip before the
 // dense contraction ("Platforms and accelerators": weights dequantized in
 // threadgroup memory).  On gfx950 the dense step is the fp16 matrix-core
-// instruction v_mfma_f32_32x32x16_f16 (fp32 accumulate), so weights are
-// rounded once to fp16: RN_fp16((q - 8) * d).
+// instruction v_mfma_f32_32x32x16_f16 (fp32 accumulate).  Q4_0 and Q8_0
+// weights are rounded once to fp16: RN_fp16((q - 8) * d), RN_fp16(c * d).
+// int8 block-64 scales are fp32, not fp16 values: the B tile holds the exact
+// codes, the two steps of a 64-element unit accumulate into a second set of
+// accumulators, and the unit's scale multiplies that block sum in fp32.
 //
 // Design for gfx950 (measured here: ds_read_b128 ~220 B/clk/CU, fp16 MFMA
 // ~36 cycles per 32x32x16 instruction, and a wave's vector ALU work does not
@@ -62,7 +66,9 @@ constexpr int kXRowBytes = 64;
 // loads and kOthers code / scale / spare loads per step.
 template <int FMT, int NT>
 struct Cfg {
-    static constexpr int P = FMT == kQ8_0 ? 2 : 1;                // 16-byte code parts per unit
+    static constexpr int P = FMT == kQ4_0 ? 1 : 2;                // 16-byte code parts per row per step
+    static constexpr int SB = FMT == kI8B64 ? 4 : 2;              // scale bytes
+    static constexpr int SPS = FMT == kI8B64 ? 2 : 1;             // steps per scale block
     static constexpr int BN = 64 * NT;
     static constexpr int kStages = (P == 2 && NT == 3) ? 5 : 6;   // copies run kStages - 2 steps ahead
     static constexpr int kOthers = (NT * P + NT + kWaves - 1) / kWaves;
@@ -76,6 +82,7 @@ struct Cfg {
     static constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;     // <= 159,744
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
     static_assert(kStages >= 5, "the unpack needs step st + 2 landed");
+    static_assert(FMT != kI8B64 || NT == 2, "int8 block-64 keeps a second accumulator set");
 };
 
 // Output tiles below which K is split across workgroups, and the workgroups
@@ -87,7 +94,7 @@ constexpr int kSplitTargetWgs = 256;
 // K; its workgroups are wg0 .. wg0 + tiles_m * tiles_n * S - 1.
 struct GemmMat {
     const uint8_t* codes;     // code plane (tiled layout)
-    const uint16_t* scales;   // scale plane (tiled layout)
+    const uint8_t* scales;    // scale plane (tiled layout; fp16, or fp32 for int8 block-64)
     float* out;               // Y (S == 1) or S partial M x N slices
     int32_t N, tiles_n, wg0, pad;
 };
@@ -96,7 +103,7 @@ struct GemmArgs {
     GemmMat mat[kMaxGemmGroup];
     const _Float16* X;        // M x K row-major
     int32_t count;            // matrices
-    int32_t M, K, nu;         // nu = K / 32
+    int32_t M, K, nu;         // nu = K / 32 (steps)
     int32_t tiles_m, S, us;   // us: blocks per K slice
     int32_t remap;            // 1: XCD-aware workgroup order
 };
@@ -116,6 +123,12 @@ __device__ __forceinline__ uint32_t w2(uint32_t v, uint32_t sel, half2_t dd) {
 __device__ __forceinline__ uint32_t w8(uint32_t v, uint32_t sel, half2_t dd) {
     const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
     return bits((as_half2(__builtin_amdgcn_perm(0x64646464u, v, sel)) - off) * dd);
+}
+
+// Two exact fp16 int8 codes from two sign-flipped codes (bytes `sel` of v).
+__device__ __forceinline__ uint32_t wi8(uint32_t v, uint32_t sel) {
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return bits(as_half2(__builtin_amdgcn_perm(0x64646464u, v, sel)) - off);
 }
 
 // LDS byte offset of 16-byte chunk `chunk` (0-3) of a 64-byte row (an X row
@@ -189,9 +202,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
     }
     constexpr int kOthers = C::kOthers;
     const uint8_t* osrc[kOthers];   // per-lane source of the step-0 block
-    uint32_t ostep[kOthers];        // source bytes per step
+    uint32_t ostep[kOthers];        // source bytes per step (per scale block for scales)
     uint32_t odst[kOthers];         // LDS offset inside the slot
-    int osize[kOthers];             // 16 (codes) or 2 (scales)
+    int osize[kOthers];             // 16 (codes) or the scale size
+    int oshift[kOthers];            // step -> source block: st >> oshift
 #pragma unroll
     for (int k = 0; k < kOthers; ++k) {
         const int q = wave + kWaves * k;
@@ -206,12 +220,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
             ostep[k] = uint32_t(P * lnr * 16);
             odst[k] = uint32_t(C::kWOff + q * 1024);
             osize[k] = 16;
+            oshift[k] = 0;
         } else {
-            osrc[k] = reinterpret_cast<const uint8_t*>(G.scales + size_t(ltb) * kTileRows * size_t(a.nu) +
-                                                       size_t(u0) * lnr + lrow);
-            ostep[k] = uint32_t(lnr * 2);
+            // One scale per row and scale block (SPS steps); both steps of an
+            // int8 block-64 unit copy its scales.
+            const size_t blocks = size_t(a.nu) / C::SPS;
+            osrc[k] = G.scales + (size_t(ltb) * kTileRows * blocks + size_t(u0 / C::SPS) * lnr + lrow) * C::SB;
+            ostep[k] = uint32_t(lnr * C::SB);
             odst[k] = uint32_t(q < NT * P + NT ? C::kSOff + t * 256 : C::kDummyOff);
-            osize[k] = 2;
+            osize[k] = C::SB;
+            oshift[k] = C::SPS == 2 ? 1 : 0;
         }
     }
     auto issue = [&](int st) {   // loads of step st into slot st % kStages
@@ -224,12 +242,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
                 (__attribute__((address_space(3))) void*)(slot + (2 * wave + i) * 1024), 16, 0, 0);
 #pragma unroll
         for (int k = 0; k < kOthers; ++k) {
-            const auto* src = (const __attribute__((address_space(1))) void*)(osrc[k] + size_t(st) * ostep[k]);
+            const auto* src =
+                (const __attribute__((address_space(1))) void*)(osrc[k] + size_t(st >> oshift[k]) * ostep[k]);
             auto* dst = (__attribute__((address_space(3))) void*)(slot + odst[k]);
             // The copy size must be an immediate: the 16-byte (codes) or
-            // 2-byte (scales) form, chosen per wave.
+            // scale-size form, chosen per wave.
             if (osize[k] == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-            else __builtin_amdgcn_global_load_lds(src, dst, 2, 0, 0);
+            else __builtin_amdgcn_global_load_lds(src, dst, C::SB, 0, 0);
         }
     };
 
@@ -264,10 +283,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
 #pragma unroll
         for (int q = 0; q < kTasks; ++q) {
             const u32x2 c = *reinterpret_cast<const u32x2*>(slot + uc_off[q]);
+            u32x4 v;
+            if constexpr (FMT == kI8B64) {
+                // Exact codes; the fp32 scale multiplies the block sums.
+                const uint32_t b0 = c.x ^ 0x80808080u, b1 = c.y ^ 0x80808080u;
+                v = u32x4{wi8(b0, 0x04010400u), wi8(b0, 0x04030402u), wi8(b1, 0x04010400u), wi8(b1, 0x04030402u)};
+                *reinterpret_cast<u32x4*>(btile + ub_off[q]) = v;
+                continue;
+            }
             const uint16_t d = *reinterpret_cast<const uint16_t*>(slot + us_off[q]);
             const _Float16 dh = __builtin_bit_cast(_Float16, d);
             const half2_t dd = {dh, dh};
-            u32x4 v;
             if constexpr (P == 1) {
                 const uint32_t n0 = (c.x >> ush[q]) & 0x0F0F0F0Fu, n1 = (c.y >> ush[q]) & 0x0F0F0F0Fu;
                 v = u32x4{w2(n0, 0x04010400u, dd), w2(n0, 0x04030402u, dd), w2(n1, 0x04010400u, dd),
@@ -330,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
         lds_barrier();
         read_frags(0);
     }
-    for (int st = 0; st < nst; ++st) {
+    auto step = [&](int st, f32x16 (&dst)[2][NT]) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 4) * kLoadsPerStep));   // step st + 2 landed
         lds_barrier();
         issue(min(st + kStages - 1, nst - 1));
@@ -350,7 +376,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[s][i], b0[s][j], acc[i][j], 0, 0, 0);
+                    dst[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[s][i], b0[s][j], dst[i][j], 0, 0, 0);
+    };
+    if constexpr (FMT == kI8B64) {
+        // The two steps of a 64-element unit accumulate exact-code products
+        // into blk; the unit's fp32 scale of column n (this lane's column in
+        // every accumulator register) then multiplies the block sum, read
+        // from the second step's slot (both steps copy the unit's scales).
+        // Slices hold whole units, so nst is even.
+        const uint32_t s_off[NT] = {uint32_t(C::kSOff + wn * 256 + (lane & 31) * 4),
+                                    uint32_t(C::kSOff + wn * 256 + (32 + (lane & 31)) * 4)};
+        for (int st = 0; st < nst; st += 2) {
+            f32x16 blk[2][NT];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) blk[i][j][r] = 0.0f;
+            step(st, blk);
+            step(st + 1, blk);
+            const uint8_t* slot = slot_of(st + 1);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const float sc = *reinterpret_cast<const float*>(slot + s_off[j]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[i][j] = __builtin_elementwise_fma(f32x16(sc), blk[i][j], acc[i][j]);
+            }
+        }
+    } else {
+        for (int st = 0; st < nst; ++st) step(st, acc);
     }
 
     // ---- epilogue: straight from the accumulators.  32x32 accumulator
@@ -404,7 +460,9 @@ struct Plan {
     int64_t wgs;
 };
 
-Plan plan_for(int nt, int64_t M, const int64_t* N, int count, int64_t K) {
+// sps: steps per scale block (2 for int8 block-64: a K slice holds whole
+// 64-element units).
+Plan plan_for(int nt, int64_t M, const int64_t* N, int count, int64_t K, int sps) {
     Plan p;
     p.nt = nt;
     p.tiles_m = int((M + BM - 1) / BM);
@@ -415,17 +473,18 @@ Plan plan_for(int nt, int64_t M, const int64_t* N, int count, int64_t K) {
     if (count == 1 && tiles < kSplitBelowTiles) S = int(std::max<int64_t>(1, kSplitTargetWgs / tiles));
     S = std::min(S, std::max(1, nu / 16));   // at least 16 blocks (steps) per slice
     const int us = (nu + S - 1) / S;
-    p.us = us;
-    p.S = (nu + us - 1) / us;                // no empty slice
+    p.us = (us + sps - 1) / sps * sps;
+    p.S = (nu + p.us - 1) / p.us;            // no empty slice
     p.wgs = tiles * p.S;
     return p;
 }
 
-Plan plan_gemm(int64_t M, const int64_t* N, int count, int64_t K, int cus) {
+Plan plan_gemm(int fmt, int64_t M, const int64_t* N, int count, int64_t K, int cus) {
+    if (fmt == kI8B64) return plan_for(2, M, N, count, K, 2);
 #ifdef LQ_GEMM_NT_ONLY
-    return plan_for(LQ_GEMM_NT_ONLY, M, N, count, K);
+    return plan_for(LQ_GEMM_NT_ONLY, M, N, count, K, 1);
 #endif
-    const Plan p2 = plan_for(2, M, N, count, K), p3 = plan_for(3, M, N, count, K);
+    const Plan p2 = plan_for(2, M, N, count, K, 1), p3 = plan_for(3, M, N, count, K, 1);
     if (p3.S > 1) return p2;
     const int64_t c = std::max(cus, 1);
     const int64_t w2 = (p2.wgs + c - 1) / c * 2 * p2.us, w3 = (p3.wgs + c - 1) / c * 3 * p3.us;
@@ -454,11 +513,11 @@ hipError_t launch_tile(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
     // Whichever tile width the launch picks (that depends on the CU count).
     size_t need = 0;
-    for (int nt = 2; nt <= 3; ++nt) {
-        const Plan p = plan_for(nt, M, &N, 1, K);
+    for (int nt = 2; nt <= (fmt == kI8B64 ? 2 : 3); ++nt) {
+        const Plan p = plan_for(nt, M, &N, 1, K, fmt == kI8B64 ? 2 : 1);
         if (p.S > 1) need = std::max(need, size_t(p.S) * size_t(M) * size_t(N) * sizeof(float));
     }
     return need;
@@ -473,15 +532,14 @@ hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipS
 hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, const int64_t* N, int count,
                             const void* X, int64_t M, int64_t K, void* ws, int cus, hipStream_t stream) {
     if (count < 1 || count > kMaxGemmGroup) return hipErrorInvalidValue;
-    if (fmt != kQ4_0 && fmt != kQ8_0) return hipErrorInvalidValue;
-    const Plan p = plan_gemm(M, N, count, K, cus);
+    if (fmt != kQ4_0 && fmt != kQ8_0 && fmt != kI8B64) return hipErrorInvalidValue;
+    const Plan p = plan_gemm(fmt, M, N, count, K, cus);
     GemmArgs a = {};
     int64_t wgs = 0;
     for (int i = 0; i < count; ++i) {
         GemmMat& g = a.mat[i];
         g.codes = static_cast<const uint8_t*>(W[i]);
-        g.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(W[i]) +
-                                                     align256(code_plane_bytes(fmt, N[i], K)));
+        g.scales = static_cast<const uint8_t*>(W[i]) + align256(code_plane_bytes(fmt, N[i], K));
         g.out = p.S > 1 ? static_cast<float*>(ws) : Y[i];
         g.N = int32_t(N[i]);
         g.tiles_n = int32_t((N[i] + 64 * p.nt - 1) / (64 * p.nt));
@@ -501,7 +559,8 @@ hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, cons
     a.remap = (wgs % 8 == 0) ? 1 : 0;
     hipError_t e;
     if (fmt == kQ4_0) e = p.nt == 3 ? launch_tile<kQ4_0, 3>(a, wgs, stream) : launch_tile<kQ4_0, 2>(a, wgs, stream);
-    else e = p.nt == 3 ? launch_tile<kQ8_0, 3>(a, wgs, stream) : launch_tile<kQ8_0, 2>(a, wgs, stream);
+    else if (fmt == kQ8_0) e = p.nt == 3 ? launch_tile<kQ8_0, 3>(a, wgs, stream) : launch_tile<kQ8_0, 2>(a, wgs, stream);
+    else e = launch_tile<kI8B64, 2>(a, wgs, stream);
     if (e != hipSuccess || p.S == 1) return e;
     return launch_splitk_reduce(static_cast<const float*>(ws), Y[0], size_t(M) * size_t(N[0]), p.S, stream);
 }

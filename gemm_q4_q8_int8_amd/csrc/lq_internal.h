@@ -209,18 +209,13 @@ hipError_t launch_dequant(int fmt, bool to_f16, const void* W, void* out, int64_
 constexpr int kMaxGemmGroup = 4;
 // Split-K workspace of a single-matrix launch (0: none).  Launches of
 // several matrices never split K.
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
-// Q4_0 and Q8_0: weights dequantized to fp16 tiles in LDS.
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+// Weights decoded to fp16 tiles in LDS: Q4_0 and Q8_0 as RN_fp16(q d),
+// int8 block-64 as exact codes with the fp32 scale applied to block sums.
 hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, const int64_t* N, int count,
                             const void* X, int64_t M, int64_t K, void* ws, int num_cus,
                             hipStream_t stream);
 // Y = sum of S partial M x N slices (slice order), for split-K GEMMs.
 hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipStream_t stream);
-
-// Prefill GEMM for Q8_0 and int8 block-64 (codes straight from the packed
-// layout into matrix-core operands).
-size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t launch_prefill(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t N,
-                          int64_t K, void* ws, hipStream_t stream);
 
 }  // namespace lq

@@ -266,13 +266,11 @@ typedef struct lq_gemm_desc {
  * FFN over the same prompt chunk: for each descriptor, Y = X W^T as lq_gemm
  * computes it (the same fp16 weight tile and products, with the same
  * accuracy; the same bits whenever lq_gemm needs no workspace for that matrix
- * alone, i.e. does not split its K).  LQ_Q4_0 and LQ_Q8_0 run all of them
- * in one kernel launch, so their output tiles fill the GPU together;
- * LQ_I8B64 runs one launch per matrix, in order.  descs: HOST array, read
+ * alone, i.e. does not split its K).  All of them run in one kernel launch,
+ * so their output tiles fill the GPU together.  descs: HOST array, read
  * during the call only; everything is validated before anything is enqueued.
  * ws / ws_bytes: a workspace of the largest lq_gemm_workspace_bytes() over
- * the descriptors suffices (an LQ_Q4_0 or LQ_Q8_0 call with count > 1 needs
- * none). */
+ * the descriptors suffices (a call with count > 1 needs none). */
 lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int64_t K,
                         const lq_gemm_desc* descs, int32_t count,
                         void* ws, size_t ws_bytes, void* stream);

@@ -2,9 +2,8 @@
 
 Each descriptor's Y must be what lq_gemm gives for that matrix alone (the
 same bits, unless lq_gemm splits that matrix's K, which a grouped launch
-never does) and within the GEMM bar of the exact product.  Q4_0 and Q8_0 run
-a group as one launch, which can pick the
-wider 192-row weight tile when the narrower one would need a second round of
+never does) and within the GEMM bar of the exact product.  Every format runs
+a group as one launch; Q4_0 and Q8_0 can pick the wider 192-row weight tile when the narrower one would need a second round of
 workgroups (e.g. M = 512 over two 8200-row or two 11008-row matrices on a
 256-CU part); the shapes below cover that path, ragged N (not a multiple of
 64 or of 192), ragged M, and K of a few blocks (fewer steps than the copy
@@ -60,6 +59,8 @@ GROUPS = [
     ("q8_0", 40, [70, 300], 512),
     ("q8_0", 512, [8200, 8264], 128),         # Q8_0 on the 192-row tile (five-slot copy ring)
     ("i8b64", 33, [256, 65], 1024),
+    ("i8b64", 512, [8200, 8264], 128),        # two 64-element units per row
+    ("i8b64", 300, [64, 1000, 33, 4100], 192),  # four matrices, an odd number of units
 ]
 
 
@@ -75,7 +76,7 @@ def test_batch_parity_and_same_bits_as_single(oracle, fmt, M, Ns, K):
         # Same bits as lq_gemm alone unless that splits K (a grouped Q4_0 /
         # Q8_0 launch never does); within the bar either way.
         single = gu.gemm(W1, X, M, N, K, fmt)
-        if fmt == "i8b64" or len(Ns) == 1 or lq.lq_gemm_workspace_bytes(gu.FMT[fmt], M, N, K) == 0:
+        if len(Ns) == 1 or lq.lq_gemm_workspace_bytes(gu.FMT[fmt], M, N, K) == 0:
             assert np.array_equal(Y.view(np.uint32), single.view(np.uint32)), (fmt, M, N, K, "differs from lq_gemm")
         ms, ns = sample(M, N, rng, (255, 256), (63, 64, 127, 128, 191, 192))
         Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K, ms=ms, ns=ns)
