@@ -15,9 +15,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblq.so")
 
-LQ_Q4_0, LQ_Q8_0, LQ_I8B64 = 0, 1, 2
+LQ_Q4_0, LQ_Q8_0, LQ_I8B64, LQ_I8B32 = 0, 1, 2, 3
 LQ_F32, LQ_F16, LQ_BF16 = 0, 1, 2
-FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64}
+FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64, "i8b32": LQ_I8B32}
 
 # Every symbol include/lq.h declares.
 EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq_scale_offset",

@@ -26,7 +26,8 @@ lq_status hip_fail(hipError_t e, const char* what) {
     return fail(LQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool fmt_ok(int32_t f) { return f == LQ_Q4_0 || f == LQ_Q8_0 || f == LQ_I8B64; }
+bool fmt_ok(int32_t f) { return f == LQ_Q4_0 || f == LQ_Q8_0 || f == LQ_I8B64 || f == LQ_I8B32; }
+bool has_gguf_form(int32_t f) { return f == LQ_Q4_0 || f == LQ_Q8_0; }
 int32_t block_of(int32_t f) { return f == LQ_I8B64 ? 64 : (fmt_ok(f) ? 32 : 0); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 constexpr int64_t kMaxDim = 2147483647;
@@ -333,6 +334,8 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
 extern "C" {
 
 static_assert(LQ_GEMM_MAX_GROUP == lq::kMaxGemmGroup, "GEMM group size");
+static_assert(LQ_Q4_0 == lq::kQ4_0 && LQ_Q8_0 == lq::kQ8_0 && LQ_I8B64 == lq::kI8B64 && LQ_I8B32 == lq::kI8B32,
+              "format numbering");
 
 int32_t lq_abi_version(void) { return LQ_ABI_VERSION; }
 
@@ -358,13 +361,14 @@ size_t lq_scale_offset(int32_t fmt, int64_t N, int64_t K) {
 }
 
 size_t lq_gguf_bytes(int32_t fmt, int64_t N, int64_t K) {
-    if (fmt == LQ_I8B64 || check_fmt_shape(fmt, N, K) != LQ_OK) return 0;
+    if (!has_gguf_form(fmt) || check_fmt_shape(fmt, N, K) != LQ_OK) return 0;
     return size_t(N) * size_t(K / 32) * (fmt == LQ_Q4_0 ? 18 : 34);
 }
 
 lq_status lq_repack_gguf(int32_t fmt, const void* src, void* dst, int64_t N, int64_t K, void* stream) {
     LQ_TRY(check_fmt_shape(fmt, N, K));
-    if (fmt == LQ_I8B64) return fail(LQ_ERR_FMT, "LQ_I8B64 has no GGUF form; use lq_pack_planes");
+    if (fmt_ok(fmt) && !has_gguf_form(fmt))
+        return fail(LQ_ERR_FMT, "fmt=%d (int8 with fp32 scales) has no GGUF form; use lq_pack_planes", fmt);
     LQ_TRY(check_ptr(src, 2, "src"));
     LQ_TRY(check_ptr(dst, 16, "dst"));
     const hipError_t e = lq::launch_repack_gguf(fmt, src, dst, N, K, static_cast<hipStream_t>(stream));

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     }
     if (!F16) {
         float s;
-        if (FMT == kI8B64) s = reinterpret_cast<const float*>(W + scale_off)[pos.scale];
+        if (fp32_scale(FMT)) s = reinterpret_cast<const float*>(W + scale_off)[pos.scale];
         else s = float(reinterpret_cast<const _Float16*>(W + scale_off)[pos.scale]);
         f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * K + int64_t(u) * 32);
 #pragma unroll
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
         }
     } else {
         uint16_t h[32];
-        if (FMT == kI8B64) {
+        if (fp32_scale(FMT)) {
             const float s = reinterpret_cast<const float*>(W + scale_off)[pos.scale];
 #pragma unroll
             for (int j = 0; j < 32; ++j) h[j] = rn16_code_times_f32(code[j], s);
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restri
     for (int e = 0; e < E; ++e) w[e] = source_value<SDT>(src, row * K + u * E + e);
     const TiledPos pos = tiled_pos(FMT, N, nu, row, u);
     uint8_t q[E];
-    if constexpr (FMT == kI8B64) {
+    if constexpr (fp32_scale(FMT)) {
         float a = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) a = fabsf(w[e]) > a ? fabsf(w[e]) : a;
@@ -319,6 +319,7 @@ hipError_t launch_pack_planes(int fmt, const void* codes, const void* scales, vo
         case kQ4_0: hipLaunchKernelGGL(pack_kernel<kQ4_0>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
         case kQ8_0: hipLaunchKernelGGL(pack_kernel<kQ8_0>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
         case kI8B64: hipLaunchKernelGGL(pack_kernel<kI8B64>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
+        case kI8B32: hipLaunchKernelGGL(pack_kernel<kI8B32>, grid, dim3(kThreads), 0, stream, c, s, d, N, nu, off); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -341,6 +342,9 @@ hipError_t launch_quantize(int fmt, int sdt, const void* src, void* dst, int64_t
         case kI8B64 * 3 + kF32: LQ_QK(kI8B64, kF32); break;
         case kI8B64 * 3 + kF16: LQ_QK(kI8B64, kF16); break;
         case kI8B64 * 3 + kBF16: LQ_QK(kI8B64, kBF16); break;
+        case kI8B32 * 3 + kF32: LQ_QK(kI8B32, kF32); break;
+        case kI8B32 * 3 + kF16: LQ_QK(kI8B32, kF16); break;
+        case kI8B32 * 3 + kBF16: LQ_QK(kI8B32, kBF16); break;
         default: return hipErrorInvalidValue;
     }
 #undef LQ_QK
@@ -361,6 +365,8 @@ hipError_t launch_dequant(int fmt, bool to_f16, const void* W, void* out, int64_
         case kQ8_0 * 2 + 1: LQ_DQ(kQ8_0, true); break;
         case kI8B64 * 2 + 0: LQ_DQ(kI8B64, false); break;
         case kI8B64 * 2 + 1: LQ_DQ(kI8B64, true); break;
+        case kI8B32 * 2 + 0: LQ_DQ(kI8B32, false); break;
+        case kI8B32 * 2 + 1: LQ_DQ(kI8B32, true); break;
         default: return hipErrorInvalidValue;
     }
 #undef LQ_DQ

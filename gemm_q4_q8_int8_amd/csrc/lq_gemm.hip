@@ -67,8 +67,8 @@ constexpr int kXRowBytes = 64;
 template <int FMT, int NT>
 struct Cfg {
     static constexpr int P = FMT == kQ4_0 ? 1 : 2;                // 16-byte code parts per row per step
-    static constexpr int SB = FMT == kI8B64 ? 4 : 2;              // scale bytes
-    static constexpr int SPS = FMT == kI8B64 ? 2 : 1;             // steps per scale block
+    static constexpr int SB = scale_bytes(FMT);
+    static constexpr int SPS = unit_elems(FMT) / 32;              // steps per scale block
     static constexpr int BN = 64 * NT;
     static constexpr int kStages = (P == 2 && NT == 3) ? 5 : 6;   // copies run kStages - 2 steps ahead
     static constexpr int kOthers = (NT * P + NT + kWaves - 1) / kWaves;
@@ -82,7 +82,7 @@ struct Cfg {
     static constexpr int kLdsBytes = kBOff + 3 * kBTileBytes;     // <= 159,744
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
     static_assert(kStages >= 5, "the unpack needs step st + 2 landed");
-    static_assert(FMT != kI8B64 || NT == 2, "int8 block-64 keeps a second accumulator set");
+    static_assert(!fp32_scale(FMT) || NT == 2, "fp32-scale formats keep a second accumulator set");
 };
 
 // Output tiles below which K is split across workgroups, and the workgroups
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
         for (int q = 0; q < kTasks; ++q) {
             const u32x2 c = *reinterpret_cast<const u32x2*>(slot + uc_off[q]);
             u32x4 v;
-            if constexpr (FMT == kI8B64) {
+            if constexpr (fp32_scale(FMT)) {
                 // Exact codes; the fp32 scale multiplies the block sums.
                 const uint32_t b0 = c.x ^ 0x80808080u, b1 = c.y ^ 0x80808080u;
                 v = u32x4{wi8(b0, 0x04010400u), wi8(b0, 0x04030402u), wi8(b1, 0x04010400u), wi8(b1, 0x04030402u)};
@@ -378,15 +378,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
                 for (int j = 0; j < NT; ++j)
                     dst[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[s][i], b0[s][j], dst[i][j], 0, 0, 0);
     };
-    if constexpr (FMT == kI8B64) {
-        // The two steps of a 64-element unit accumulate exact-code products
-        // into blk; the unit's fp32 scale of column n (this lane's column in
-        // every accumulator register) then multiplies the block sum, read
-        // from the second step's slot (both steps copy the unit's scales).
-        // Slices hold whole units, so nst is even.
+    if constexpr (fp32_scale(FMT)) {
+        // The SPS steps of a unit (2 for 64-element units, 1 for 32)
+        // accumulate exact-code products into blk; the unit's fp32 scale of
+        // column n (this lane's column in every accumulator register) then
+        // multiplies the block sum, read from the unit's last step's slot
+        // (every step copies its unit's scales).  Slices hold whole units,
+        // so nst is a multiple of SPS.
+        constexpr int SPS = C::SPS;
         const uint32_t s_off[NT] = {uint32_t(C::kSOff + wn * 256 + (lane & 31) * 4),
                                     uint32_t(C::kSOff + wn * 256 + (32 + (lane & 31)) * 4)};
-        for (int st = 0; st < nst; st += 2) {
+        for (int st = 0; st < nst; st += SPS) {
             f32x16 blk[2][NT];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -394,9 +396,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
                 for (int j = 0; j < NT; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) blk[i][j][r] = 0.0f;
-            step(st, blk);
-            step(st + 1, blk);
-            const uint8_t* slot = slot_of(st + 1);
+#pragma unroll
+            for (int q = 0; q < SPS; ++q) step(st + q, blk);
+            const uint8_t* slot = slot_of(st + SPS - 1);
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const float sc = *reinterpret_cast<const float*>(slot + s_off[j]);
@@ -480,7 +482,7 @@ Plan plan_for(int nt, int64_t M, const int64_t* N, int count, int64_t K, int sps
 }
 
 Plan plan_gemm(int fmt, int64_t M, const int64_t* N, int count, int64_t K, int cus) {
-    if (fmt == kI8B64) return plan_for(2, M, N, count, K, 2);
+    if (fp32_scale(fmt)) return plan_for(2, M, N, count, K, unit_elems(fmt) / 32);
 #ifdef LQ_GEMM_NT_ONLY
     return plan_for(LQ_GEMM_NT_ONLY, M, N, count, K, 1);
 #endif
@@ -516,8 +518,8 @@ hipError_t launch_tile(const GemmArgs& a, int64_t grid, hipStream_t stream) {
 size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
     // Whichever tile width the launch picks (that depends on the CU count).
     size_t need = 0;
-    for (int nt = 2; nt <= (fmt == kI8B64 ? 2 : 3); ++nt) {
-        const Plan p = plan_for(nt, M, &N, 1, K, fmt == kI8B64 ? 2 : 1);
+    for (int nt = 2; nt <= (fp32_scale(fmt) ? 2 : 3); ++nt) {
+        const Plan p = plan_for(nt, M, &N, 1, K, unit_elems(fmt) / 32);
         if (p.S > 1) need = std::max(need, size_t(p.S) * size_t(M) * size_t(N) * sizeof(float));
     }
     return need;
@@ -532,7 +534,7 @@ hipError_t launch_splitk_reduce(const float* P, float* Y, size_t mn, int S, hipS
 hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, const int64_t* N, int count,
                             const void* X, int64_t M, int64_t K, void* ws, int cus, hipStream_t stream) {
     if (count < 1 || count > kMaxGemmGroup) return hipErrorInvalidValue;
-    if (fmt != kQ4_0 && fmt != kQ8_0 && fmt != kI8B64) return hipErrorInvalidValue;
+    if (fmt != kQ4_0 && fmt != kQ8_0 && fmt != kI8B64 && fmt != kI8B32) return hipErrorInvalidValue;
     const Plan p = plan_gemm(fmt, M, N, count, K, cus);
     GemmArgs a = {};
     int64_t wgs = 0;
@@ -560,7 +562,8 @@ hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, cons
     hipError_t e;
     if (fmt == kQ4_0) e = p.nt == 3 ? launch_tile<kQ4_0, 3>(a, wgs, stream) : launch_tile<kQ4_0, 2>(a, wgs, stream);
     else if (fmt == kQ8_0) e = p.nt == 3 ? launch_tile<kQ8_0, 3>(a, wgs, stream) : launch_tile<kQ8_0, 2>(a, wgs, stream);
-    else e = launch_tile<kI8B64, 2>(a, wgs, stream);
+    else if (fmt == kI8B64) e = launch_tile<kI8B64, 2>(a, wgs, stream);
+    else e = launch_tile<kI8B32, 2>(a, wgs, stream);
     if (e != hipSuccess || p.S == 1) return e;
     return launch_splitk_reduce(static_cast<const float*>(ws), Y[0], size_t(M) * size_t(N[0]), p.S, stream);
 }

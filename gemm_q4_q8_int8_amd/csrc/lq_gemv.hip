@@ -233,7 +233,7 @@ __device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, siz
         static_assert(MT == 1, "several tokens take fp16 activations");
         const cf32_p x = (cf32_p)(xv) + size_t(u) * E;
         if constexpr (FMT == kQ4_0) dot[0] = dot_q4_0_f32(b.c[0], x);
-        else if constexpr (FMT == kQ8_0) dot[0] = dot_i8_f32(b.c[0], b.c[1], x);
+        else if constexpr (unit_parts(FMT) == 2) dot[0] = dot_i8_f32(b.c[0], b.c[1], x);
         else dot[0] = dot_i8_f32(b.c[0], b.c[1], x) + dot_i8_f32(b.c[2], b.c[3], x + 32);
     } else {
         cu32_p x[MT];
@@ -241,7 +241,7 @@ __device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, siz
         for (int t = 0; t < MT; ++t) x[t] = (cu32_p)(xv) + size_t(t) * xs + size_t(u) * (E / 2);
         if constexpr (FMT == kQ4_0) {
             dot_q4_0_f16<MT>(b.c[0], x, dot);
-        } else if constexpr (FMT == kQ8_0) {
+        } else if constexpr (unit_parts(FMT) == 2) {
             dot_i8_f16<MT>(b.c[0], b.c[1], x, 0, dot);
         } else {
             float d2[MT];
@@ -252,7 +252,7 @@ __device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, siz
         }
     }
     float d;
-    if constexpr (FMT == kI8B64) d = __uint_as_float(b.s);
+    if constexpr (fp32_scale(FMT)) d = __uint_as_float(b.s);
     else d = (float)__builtin_bit_cast(_Float16, uint16_t(b.s));
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = __builtin_fmaf(d, __uint_as_float(__float_as_uint(dot[t]) & keep), acc[t]);
@@ -260,7 +260,7 @@ __device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, siz
 
 // Largest batch of units one wave loads before computing them (register
 // budget: the codes of a batch stay live).
-constexpr int unroll_cap(int fmt) { return fmt == kQ4_0 ? LQ_GEMV_UNR_Q4 : (fmt == kQ8_0 ? LQ_GEMV_UNR_Q8 : LQ_GEMV_UNR_I8); }
+constexpr int unroll_cap(int fmt) { return fmt == kQ4_0 ? LQ_GEMV_UNR_Q4 : (fmt == kI8B64 ? LQ_GEMV_UNR_I8 : LQ_GEMV_UNR_Q8); }
 
 // sum_{j < S} p[j * pitch] in slice order, loads issued eight at a time so
 // their latencies overlap.
@@ -671,6 +671,7 @@ hipError_t launch_gemv_sub(int fmt, int xdt, int mt, const GemvArgs& a, hipStrea
     switch (fmt) {
         case kQ8_0: return launch_sub_tokens<kQ8_0, gemv_max_tokens(kQ8_0)>(xdt, mt, a, stream);
         case kI8B64: return launch_sub_tokens<kI8B64, gemv_max_tokens(kI8B64)>(xdt, mt, a, stream);
+        case kI8B32: return launch_sub_tokens<kI8B32, gemv_max_tokens(kI8B32)>(xdt, mt, a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -681,6 +682,7 @@ hipError_t launch_gemv(int fmt, int xdt, int waves, int mt, const GemvArgs& a, h
         case kQ4_0: return launch_fmt<kQ4_0>(xdt, waves, mt, a, stream);
         case kQ8_0: return launch_fmt<kQ8_0>(xdt, waves, mt, a, stream);
         case kI8B64: return launch_fmt<kI8B64>(xdt, waves, mt, a, stream);
+        case kI8B32: return launch_fmt<kI8B32>(xdt, waves, mt, a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -9,7 +9,7 @@
 
 namespace lq {
 
-enum Fmt : int { kQ4_0 = 0, kQ8_0 = 1, kI8B64 = 2 };
+enum Fmt : int { kQ4_0 = 0, kQ8_0 = 1, kI8B64 = 2, kI8B32 = 3 };
 enum XType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // ------------------------------------------------------ packed layout ----
@@ -24,9 +24,12 @@ enum XType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // one 2- or 4-byte scale in place of a 16-byte part.
 constexpr int kTileRows = 64;
 __host__ __device__ constexpr int unit_elems(int fmt) { return fmt == kI8B64 ? 64 : 32; }
-__host__ __device__ constexpr int unit_parts(int fmt) { return fmt == kQ4_0 ? 1 : (fmt == kQ8_0 ? 2 : 4); }
+__host__ __device__ constexpr int unit_parts(int fmt) { return fmt == kQ4_0 ? 1 : (fmt == kI8B64 ? 4 : 2); }
 __host__ __device__ constexpr int unit_bytes(int fmt) { return 16 * unit_parts(fmt); }
-__host__ __device__ constexpr int scale_bytes(int fmt) { return fmt == kI8B64 ? 4 : 2; }
+// fp32 scales (int8 block-64 and block-32): the codes stay exact and the
+// scale multiplies fp32 sums; fp16 scales (Q4_0, Q8_0).
+__host__ __device__ constexpr bool fp32_scale(int fmt) { return fmt == kI8B64 || fmt == kI8B32; }
+__host__ __device__ constexpr int scale_bytes(int fmt) { return fp32_scale(fmt) ? 4 : 2; }
 
 inline size_t code_plane_bytes(int fmt, int64_t N, int64_t K) {
     return fmt == kQ4_0 ? size_t(N) * size_t(K) / 2 : size_t(N) * size_t(K);
@@ -107,7 +110,7 @@ constexpr int64_t kGemvCounters = int64_t(1) << 16;
 #define LQ_GEMV_SUB_MAX_UNITS 128
 #endif
 inline int gemv_min_units(int fmt) {
-    return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kQ8_0 ? LQ_GEMV_MIN_UNITS_Q8 : LQ_GEMV_MIN_UNITS_I8);
+    return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kI8B64 ? LQ_GEMV_MIN_UNITS_I8 : LQ_GEMV_MIN_UNITS_Q8);
 }
 // The same for the multi-token GEMV, whose split K also moves M tokens of
 // partial sums per row through the scratch area.

@@ -320,6 +320,7 @@ hipError_t launch_gemv_multi(int fmt, const MultiArgs& a, hipStream_t stream) {
         }
         case kQ8_0: hipLaunchKernelGGL((gemv_multi_kernel<kQ8_0, LQ_MULTI_UNR_Q8>), grid, block, 0, stream, a); break;
         case kI8B64: hipLaunchKernelGGL((gemv_multi_kernel<kI8B64, LQ_MULTI_UNR_I8>), grid, block, 0, stream, a); break;
+        case kI8B32: hipLaunchKernelGGL((gemv_multi_kernel<kI8B32, LQ_MULTI_UNR_Q8>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

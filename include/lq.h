@@ -22,17 +22,23 @@
  *   LQ_I8B64  symmetric int8 with block size 64 ("wgpu-llm" page, "INT8
  *             mode", --block-size 64).  int8 codes c, one fp32 scale s per 64
  *             consecutive codes of a row; w = c * s (no zero point).
+ *   LQ_I8B32  the "oxinfer" page's Q8 ("How it works": 32 weights per scale;
+ *             "Pre-quantized checkpoints": int8 codes X.q8 with fp32 scales
+ *             X.q8s).  int8 codes c, one fp32 scale s per 32 consecutive
+ *             codes of a row; w = c * s.  Every call treats it as LQ_I8B64
+ *             with 32-code blocks.
  *
  * Packed layout (what every W argument points to).  Like the split layout in
  * which the "oxinfer" page stores quantized matrices ("Pre-quantized
  * checkpoints": codes and scales as separate tensors, in the kernels'
  * in-memory layout), a packed matrix is a code plane followed by a scale
  * plane, both in the order the GPU kernels read them.
- *   A unit is one scale block of one row: 32 weights (LQ_Q4_0, LQ_Q8_0) or 64
- *   (LQ_I8B64), with nu = K / (unit weights) units per row.  Its codes are
- *   P parts of 16 bytes: P = 1 (Q4_0: 16 bytes in GGUF byte order), 2 (Q8_0:
- *   32 int8) or 4 (LQ_I8B64: 64 int8); part p holds the unit's code bytes
- *   16p .. 16p + 15.  Its scale is fp16 (Q4_0, Q8_0) or fp32 (LQ_I8B64).
+ *   A unit is one scale block of one row: 32 weights (LQ_Q4_0, LQ_Q8_0,
+ *   LQ_I8B32) or 64 (LQ_I8B64), with nu = K / (unit weights) units per row.
+ *   Its codes are P parts of 16 bytes: P = 1 (Q4_0: 16 bytes in GGUF byte
+ *   order), 2 (Q8_0, LQ_I8B32: 32 int8) or 4 (LQ_I8B64: 64 int8); part p
+ *   holds the unit's code bytes 16p .. 16p + 15.  Its scale is fp16 (Q4_0,
+ *   Q8_0) or fp32 (LQ_I8B64, LQ_I8B32).
  *   Rows are grouped in tiles of 64: tile t holds rows 64t .. 64t + nr - 1
  *   with nr = min(64, N - 64t).  For row n = 64t + r and unit u:
  *     code part p at byte   16 * (64 t nu P + (u P + p) nr + r)
@@ -42,7 +48,8 @@
  *   code plane is N K / 2 bytes (Q4_0) or N K bytes; the scale plane starts
  *   at lq_scale_offset(), the code-plane size rounded up to 256 bytes.  The
  *   weight bytes equal those of the GGUF form (18 or 34 bytes per 32
- *   weights; 68 bytes per 64 for LQ_I8B64) plus at most 255 bytes of
+ *   weights; 68 bytes per 64 for LQ_I8B64, 36 per 32 for LQ_I8B32) plus at
+ *   most 255 bytes of
  *   padding between the planes (left as allocated).
  *
  * Conventions for every call.
@@ -58,7 +65,7 @@
  *     Calls only enqueue work (no implicit synchronisation); results are
  *     ready when the stream reaches that point.
  *   - Sizes are int64_t: N, K, M >= 1; N <= 2^31 - 1, M <= 2^31 - 1,
- *     K <= 2^25.  K must be a multiple of the format's block (32, 32, 64).
+ *     K <= 2^25.  K must be a multiple of the format's block (32, 32, 64, 32).
  *   - Alignment: W, x, X, dst, out and codes must be 16-byte aligned; y, Y
  *     and scales 4-byte aligned; src (GGUF bytes) 2-byte aligned.
  *   - Activations: x / X are fp32 (LQ_F32) or fp16 (LQ_F16), contiguous; X is
@@ -84,9 +91,9 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 5
+#define LQ_ABI_VERSION 6
 
-typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2 } lq_fmt;
+typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2, LQ_I8B32 = 3 } lq_fmt;
 /* Activation and source dtypes.  LQ_BF16 is accepted only as the source of
  * lq_quantize. */
 typedef enum lq_dtype { LQ_F32 = 0, LQ_F16 = 1, LQ_BF16 = 2 } lq_dtype;
@@ -111,7 +118,7 @@ int32_t lq_abi_version(void);
  * first use; calling this first is optional. */
 lq_status lq_init(void);
 
-/* Weights per block of `fmt` (32, 32, 64); 0 for an unknown format. */
+/* Weights per block of `fmt` (32, 32, 64, 32); 0 for an unknown format. */
 int32_t lq_block_elems(int32_t fmt);
 
 /* Bytes of the packed layout above for an N x K matrix; 0 if fmt, N or K is
@@ -122,29 +129,30 @@ size_t lq_packed_bytes(int32_t fmt, int64_t N, int64_t K);
 size_t lq_scale_offset(int32_t fmt, int64_t N, int64_t K);
 
 /* Bytes of the GGUF array-of-blocks form (18 or 34 bytes per block); 0 for
- * LQ_I8B64 (no GGUF form) or invalid arguments. */
+ * LQ_I8B64 and LQ_I8B32 (no GGUF form) or invalid arguments. */
 size_t lq_gguf_bytes(int32_t fmt, int64_t N, int64_t K);
 
 /* GGUF array-of-blocks -> packed layout (a byte permutation, no arithmetic).
  * src: N*K/32 GGUF blocks, each the fp16 scale (little-endian) followed by
  * the codes, as a GGUF reader holds them ("lean" page: the engine reads
- * quantized GGUF files).  dst: lq_packed_bytes() bytes.  LQ_I8B64 returns
- * LQ_ERR_FMT: it has no GGUF form (use lq_pack_planes). */
+ * quantized GGUF files).  dst: lq_packed_bytes() bytes.  LQ_I8B64 and
+ * LQ_I8B32 return LQ_ERR_FMT: they have no GGUF form (use lq_pack_planes). */
 lq_status lq_repack_gguf(int32_t fmt, const void* src, void* dst,
                          int64_t N, int64_t K, void* stream);
 
 /* Row-major code and scale planes -> packed layout (a byte permutation).
  * codes: the units' code bytes row by row, unit by unit (N * K / 2 bytes for
- * Q4_0 in GGUF byte order, N * K int8 for Q8_0 and LQ_I8B64); scales: one
- * per unit in the same order, N * K / 32 fp16 (Q4_0, Q8_0) or N * K / 64
- * fp32 (LQ_I8B64).  This is the "oxinfer" page's split form ("Pre-quantized
+ * Q4_0 in GGUF byte order, N * K int8 otherwise); scales: one per unit in
+ * the same order, N * K / 32 fp16 (Q4_0, Q8_0), N * K / 64 fp32 (LQ_I8B64)
+ * or N * K / 32 fp32 (LQ_I8B32).  This is the "oxinfer" page's split form ("Pre-quantized
  * checkpoints": X.q4 + X.q4s, X.q8 + X.q8s). */
 lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales,
                          void* dst, int64_t N, int64_t K, void* stream);
 
 /* Unpacked weights: out[n*K + k] = RN_fp32(w[n,k]).  Exact for Q4_0 and Q8_0
  * (the product of a small integer and an fp16 scale fits fp32); one IEEE
- * rounding of c * s for LQ_I8B64.  out: N*K fp32, 16-byte aligned. */
+ * rounding of c * s for LQ_I8B64 and LQ_I8B32.  out: N*K fp32, 16-byte
+ * aligned. */
 lq_status lq_dequant_f32(int32_t fmt, const void* W, float* out,
                          int64_t N, int64_t K, void* stream);
 
@@ -164,7 +172,8 @@ lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out,
  *   LQ_Q8_0:  a = max |w|; d = fp16(a / 127); c = clamp(rint(w / d), -127, 127)
  *   LQ_Q4_0:  m = the first w of largest |w|; d = fp16(m / -8);
  *             q = clamp(rint(w / d), -8, 7) + 8  (m itself becomes code 0)
- *   LQ_I8B64: a = max |w|; s = a / 127 (fp32);   c = clamp(rint(w / s), -127, 127)
+ *   LQ_I8B64, LQ_I8B32 (64- or 32-code blocks):
+ *             a = max |w|; s = a / 127 (fp32);   c = clamp(rint(w / s), -127, 127)
  * A zero scale gives zero weights.  Non-finite inputs give unspecified codes.
  * lq_dequant_f32 of the result is within |d| / 2 of w per element (|d| for
  * Q4_0 codes clamped at 15). */
@@ -200,7 +209,7 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
  *   Y[m, n] = sum_k w[n,k] * X[m,k]   for m < M, n < N,
  * every weight read once for all M tokens.  The weights are decoded exactly
  * (fp16 x exact integer code, fp32 block sums), the block scale applied in
- * fp32: for M <= 2 (LQ_Q4_0) or M <= 4 (LQ_Q8_0, LQ_I8B64) as lq_gemv does
+ * fp32: for M <= 2 (LQ_Q4_0) or M <= 4 (the int8-coded formats) as lq_gemv does
  * it, each token row then being lq_gemv of that row (fp16 x) bit for bit;
  * for more tokens on the matrix cores.  W: packed N x K; X: M x K fp16
  * row-major (xdt must be LQ_F16, else LQ_ERR_UNSUPPORTED); Y: M x N fp32
@@ -237,11 +246,11 @@ size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 
 /* Prefill GEMM ("oxinfer" page, "Performance": prefill is compute bound;
  * "Platforms and accelerators": weights dequantized on chip for a dense tile
- * product), all three formats, fp16 X (xdt must be LQ_F16, else
+ * product), every format, fp16 X (xdt must be LQ_F16, else
  * LQ_ERR_UNSUPPORTED), products and sums in fp32 on the matrix cores:
  *   LQ_Q4_0, LQ_Q8_0:  Y[m,n] = sum_k RN_fp16(w[n,k]) * X[m,k]
  *                      (the fp16 tile of lq_dequant_f16);
- *   LQ_I8B64:          Y[m,n] = sum_blocks s * sum_k c[n,k] * X[m,k]
+ *   LQ_I8B64, LQ_I8B32: Y[m,n] = sum_blocks s * sum_k c[n,k] * X[m,k]
  *                      (codes exact, fp32 scale applied to block sums).
  * W: packed N x K; X: M x K fp16 row-major; Y: M x N fp32 row-major.
  * ws / ws_bytes: workspace of at least lq_gemm_workspace_bytes() bytes (may

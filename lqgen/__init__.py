@@ -27,7 +27,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-Q4_0, Q8_0, I8B64 = "q4_0", "q8_0", "i8b64"
+Q4_0, Q8_0, I8B64, I8B32 = "q4_0", "q8_0", "i8b64", "i8b32"
 
 
 def splitmix64(seed: int, n: int, start: int = 0) -> np.ndarray:
@@ -107,9 +107,15 @@ def q8_0_aos(seed: int, N: int, K: int, c: float = 0.005) -> np.ndarray:
 
 def i8b64_planes(seed: int, N: int, K: int, c: float = 0.003):
     """int8 block-64 planes: codes (N*K int8, -127..127), scales (N*K/64 fp32)."""
-    assert K % 64 == 0
+    return i8_planes(seed, N, K, 64, c)
+
+
+def i8_planes(seed: int, N: int, K: int, block: int, c: float = 0.003):
+    """int8 planes with fp32 scales per `block` codes of a row: codes (N*K
+    int8, -127..127), scales (N*K/block fp32)."""
+    assert K % block == 0
     codes = int8_sym127(seed * 2, N * K)
-    scales = fp32_scales(seed * 2 + 1, N * (K // 64), c)
+    scales = fp32_scales(seed * 2 + 1, N * (K // block), c)
     return codes, scales
 
 
@@ -146,12 +152,12 @@ class Mat:
             return q4_0_aos(self.seed, self.N, self.K, self.scale_c), None
         if self.fmt == Q8_0:
             return q8_0_aos(self.seed, self.N, self.K, self.scale_c), None
-        return i8b64_planes(self.seed, self.N, self.K, self.scale_c)
+        return i8_planes(self.seed, self.N, self.K, 64 if self.fmt == I8B64 else 32, self.scale_c)
 
     @property
     def packed_bytes(self) -> int:
         """Bytes of weight data (codes + scales); identical for GGUF and planes."""
-        per = {Q4_0: 18 / 32, Q8_0: 34 / 32, I8B64: 68 / 64}[self.fmt]
+        per = {Q4_0: 18 / 32, Q8_0: 34 / 32, I8B64: 68 / 64, I8B32: 36 / 32}[self.fmt]
         return int(self.N * self.K * per)
 
 

@@ -69,6 +69,7 @@ int block_elems(int fmt) {
         case LQREF_Q4_0: return 32;
         case LQREF_Q8_0: return 32;
         case LQREF_I8B64: return 64;
+        case LQREF_I8B32: return 32;
         default: return 0;
     }
 }
@@ -80,6 +81,10 @@ int gguf_block_bytes(int fmt) {
         default: return 0;
     }
 }
+
+// The int8 formats with fp32 scales are stored as two planes (codes, scales)
+// instead of GGUF blocks.
+bool planar(int fmt) { return fmt == LQREF_I8B64 || fmt == LQREF_I8B32; }
 
 bool shape_ok(int fmt, int64_t N, int64_t K) {
     const int be = block_elems(fmt);
@@ -112,13 +117,15 @@ void decode_q8_0_block(const uint8_t* b, double out[32]) {
 // Decode row n of a matrix into out[0..K).
 void decode_row(int fmt, const uint8_t* w, const void* scales, int64_t K,
                 int64_t n, double* out) {
-    if (fmt == LQREF_I8B64) {
-        // I8B64: codes row-major N x K; one fp32 scale per 64 codes of a row;
-        // w = c * s, exact in double (8-bit times 24-bit significand).
+    if (planar(fmt)) {
+        // I8B64 / I8B32: codes row-major N x K; one fp32 scale per E = 64 or
+        // 32 codes of a row; w = c * s, exact in double (8-bit times 24-bit
+        // significand).
+        const int64_t E = block_elems(fmt);
         const int8_t* c = reinterpret_cast<const int8_t*>(w) + n * K;
-        const float* s = static_cast<const float*>(scales) + n * (K / 64);
+        const float* s = static_cast<const float*>(scales) + n * (K / E);
         for (int64_t k = 0; k < K; ++k)
-            out[k] = static_cast<double>(c[k]) * static_cast<double>(s[k / 64]);
+            out[k] = static_cast<double>(c[k]) * static_cast<double>(s[k / E]);
         return;
     }
     const int64_t nb = K / 32;
@@ -169,7 +176,7 @@ int lqref_gguf_block_bytes(int fmt) { return gguf_block_bytes(fmt); }
 int lqref_dequant(int fmt, const uint8_t* w, const void* scales, int64_t N,
                   int64_t K, double* out) {
     if (!shape_ok(fmt, N, K) || !w || !out) return -1;
-    if (fmt == LQREF_I8B64 && !scales) return -1;
+    if (planar(fmt) && !scales) return -1;
     for (int64_t n = 0; n < N; ++n) decode_row(fmt, w, scales, K, n, out + n * K);
     return 0;
 }
@@ -177,7 +184,7 @@ int lqref_dequant(int fmt, const uint8_t* w, const void* scales, int64_t N,
 int lqref_dequant_f32(int fmt, const uint8_t* w, const void* scales, int64_t N,
                       int64_t K, float* out) {
     if (!shape_ok(fmt, N, K) || !w || !out) return -1;
-    if (fmt == LQREF_I8B64 && !scales) return -1;
+    if (planar(fmt) && !scales) return -1;
     std::vector<double> row(static_cast<size_t>(K));
     for (int64_t n = 0; n < N; ++n) {
         decode_row(fmt, w, scales, K, n, row.data());
@@ -190,7 +197,7 @@ int lqref_dequant_f32(int fmt, const uint8_t* w, const void* scales, int64_t N,
 int lqref_dequant_f16(int fmt, const uint8_t* w, const void* scales, int64_t N,
                       int64_t K, uint16_t* out) {
     if (!shape_ok(fmt, N, K) || !w || !out) return -1;
-    if (fmt == LQREF_I8B64 && !scales) return -1;
+    if (planar(fmt) && !scales) return -1;
     std::vector<double> row(static_cast<size_t>(K));
     for (int64_t n = 0; n < N; ++n) {
         decode_row(fmt, w, scales, K, n, row.data());
@@ -272,14 +279,14 @@ int lqref_quantize(int fmt, const void* src, int sdt, int64_t N, int64_t K,
                    uint8_t* out, float* scales) {
     if (!shape_ok(fmt, N, K) || !src || !out) return -1;
     if (sdt != LQREF_F32 && sdt != LQREF_F16 && sdt != LQREF_BF16) return -1;
-    if (fmt == LQREF_I8B64 && !scales) return -1;
+    if (planar(fmt) && !scales) return -1;
     const int E = block_elems(fmt);
     const int64_t nb = K / E;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < nb; ++b) {
             float w[64];
             for (int e = 0; e < E; ++e) w[e] = source_at(src, sdt, n * K + b * E + e);
-            if (fmt == LQREF_I8B64) {
+            if (planar(fmt)) {
                 float a = 0.0f;
                 for (int e = 0; e < E; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;
                 const float s = a / 127.0f;
@@ -321,7 +328,7 @@ int lqref_gemv(int fmt, const uint8_t* w, const void* scales, const void* x,
                int xdt, int64_t N, int64_t K, const int64_t* rows, int64_t nrows,
                double* y, double* S, int nthreads) {
     if (!shape_ok(fmt, N, K) || !w || !x || !y || !S) return -1;
-    if (fmt == LQREF_I8B64 && !scales) return -1;
+    if (planar(fmt) && !scales) return -1;
     if (xdt != LQREF_F32 && xdt != LQREF_F16) return -1;
     if (!rows && nrows != N) return -1;
     if (rows) {
@@ -351,7 +358,7 @@ int lqref_gemm(int fmt, const uint8_t* w, const void* scales, const void* X,
                int64_t nm, const int64_t* ns, int64_t nn, int round_w_f16,
                double* Y, double* S, int nthreads) {
     if (!shape_ok(fmt, N, K) || M < 0 || !w || !X || !Y || !S || !ms || !ns) return -1;
-    if (fmt == LQREF_I8B64 && !scales) return -1;
+    if (planar(fmt) && !scales) return -1;
     if (xdt != LQREF_F32 && xdt != LQREF_F16) return -1;
     for (int64_t a = 0; a < nm; ++a) if (ms[a] < 0 || ms[a] >= M) return -1;
     for (int64_t b = 0; b < nn; ++b) if (ns[b] < 0 || ns[b] >= N) return -1;

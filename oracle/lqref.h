@@ -15,6 +15,9 @@
  *   I8B64 ("wgpu-llm" page, "INT8 mode": block size 64): symmetric int8
  *          codes, row-major N x K, one fp32 scale per 64 consecutive codes of
  *          a row; w = c * s.
+ *   I8B32 ("oxinfer" page, "How it works": Q8 with 32 weights per scale;
+ *          "Pre-quantized checkpoints": int8 codes with fp32 scales): as
+ *          I8B64 with one fp32 scale per 32 codes.
  * A matrix is N rows x K columns; blocks run along K; y = W x.
  *
  * Every function returns 0 on success and a negative value on a bad argument.
@@ -28,21 +31,22 @@
 extern "C" {
 #endif
 
-enum { LQREF_Q4_0 = 0, LQREF_Q8_0 = 1, LQREF_I8B64 = 2 };
+enum { LQREF_Q4_0 = 0, LQREF_Q8_0 = 1, LQREF_I8B64 = 2, LQREF_I8B32 = 3 };
 enum { LQREF_F32 = 0, LQREF_F16 = 1, LQREF_BF16 = 2 };
 
 /* IEEE binary16 decode (exact in double) and round-to-nearest-even encode. */
 double   lqref_half_to_double(uint16_t h);
 uint16_t lqref_double_to_half(double v);
 
-/* Weights per block, and bytes of one GGUF block (0 for I8B64, which has no
- * GGUF form). */
+/* Weights per block, and bytes of one GGUF block (0 for I8B64 and I8B32,
+ * which have no GGUF form). */
 int lqref_block_elems(int fmt);
 int lqref_gguf_block_bytes(int fmt);
 
 /* Exact decode of a whole matrix into doubles (N*K, row-major).
  * fmt Q4_0/Q8_0: w = GGUF array-of-blocks bytes, scales ignored (may be NULL).
- * fmt I8B64:     w = int8 codes (N*K), scales = fp32 plane (N*K/64). */
+ * fmt I8B64, I8B32: w = int8 codes (N*K), scales = fp32 plane (N*K/64 or
+ *                  N*K/32). */
 int lqref_dequant(int fmt, const uint8_t* w, const void* scales,
                   int64_t N, int64_t K, double* out);
 /* The same value rounded once to fp32 / to fp16 (bit patterns). */
@@ -66,12 +70,12 @@ int lqref_unpack_gguf(int fmt, const uint8_t* aos, int64_t N, int64_t K,
  *          c = clamp(rint(w / float(d)), -127, 127), 0 when d == 0.
  *   Q4_0:  m = the block's first element of largest |w|; d = fp16(m / -8);
  *          q = clamp(rint(w / float(d)) + 8, 0, 15), 8 when d == 0.
- *   I8B64: a = max |w| over the 64-block; s = a / 127 (fp32);
+ *   I8B64, I8B32: a = max |w| over the 64- or 32-block; s = a / 127 (fp32);
  *          c = clamp(rint(w / s), -127, 127), 0 when s == 0.
  * rint rounds to nearest, ties to even; fp16() rounds to nearest even.
  * src: N*K values of dtype sdt (LQREF_F32, LQREF_F16 bits, LQREF_BF16 bits),
  * finite.  Q4_0 / Q8_0: out = GGUF array-of-blocks bytes (scales unused);
- * I8B64: out = N*K int8 codes and scales = N*K/64 fp32. */
+ * I8B64 / I8B32: out = N*K int8 codes and scales = N*K/64 or N*K/32 fp32. */
 int lqref_quantize(int fmt, const void* src, int sdt, int64_t N, int64_t K,
                    uint8_t* out, float* scales);
 

@@ -16,9 +16,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lqref.cpp")
 _LIB = os.path.join(_HERE, "liblqref.so")
 
-Q4_0, Q8_0, I8B64 = 0, 1, 2
+Q4_0, Q8_0, I8B64, I8B32 = 0, 1, 2, 3
 F32, F16, BF16 = 0, 1, 2
-FMT_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0, "i8b64": I8B64}
+FMT_NAMES = {"q4_0": Q4_0, "q8_0": Q8_0, "i8b64": I8B64, "i8b32": I8B32}
+PLANAR = (I8B64, I8B32)   # int8 codes + fp32 scale plane (no GGUF form)
 
 
 def build(force: bool = True) -> str:
@@ -113,14 +114,15 @@ class Oracle:
         """Load-time quantization of a row-major N x K matrix (see lqref.h).
         src: float32 or float16 array, or uint16 bf16 bit patterns with
         sdt=BF16.  Returns (GGUF bytes, None) for Q4_0 / Q8_0 and
-        (int8 codes, fp32 scales) for I8B64, the forms the other calls take."""
+        (int8 codes, fp32 scales) for I8B64 / I8B32, the forms the other
+        calls take."""
         if sdt is None:
             sdt, src = _xdt(src)
         else:
             src = np.ascontiguousarray(src)
-        if fmt == I8B64:
+        if fmt in PLANAR:
             codes = np.empty(N * K, np.int8)
-            scales = np.empty(N * (K // 64), np.float32)
+            scales = np.empty(N * (K // self.block_elems(fmt)), np.float32)
             _check(self.L.lqref_quantize(fmt, _p(src), sdt, N, K, _p(codes), _p(scales)), "quantize")
             return codes, scales
         out = np.empty(N * (K // 32) * self.gguf_block_bytes(fmt), np.uint8)

@@ -6,7 +6,8 @@ import torch
 import gemm_q4_q8_int8_amd as lq
 from gemm_q4_q8_int8_amd.device import to_device, upload_gguf, upload_planes
 
-FMT = {"q4_0": lq.LQ_Q4_0, "q8_0": lq.LQ_Q8_0, "i8b64": lq.LQ_I8B64}
+FMT = {"q4_0": lq.LQ_Q4_0, "q8_0": lq.LQ_Q8_0, "i8b64": lq.LQ_I8B64, "i8b32": lq.LQ_I8B32}
+PLANAR = ("i8b64", "i8b32")   # int8 codes + fp32 scale planes
 GUARD = 1024            # canary floats after every output buffer
 SENTINEL = -12345.5
 
@@ -15,7 +16,7 @@ GEMM_REL, GEMM_ABS = 2e-3, 1e-5     # |Y - Y_ref| <= 2e-3 * sum|w x| + 1e-5 per 
 
 
 def upload(fmt: str, w, scales, N, K):
-    if fmt == "i8b64":
+    if fmt in PLANAR:
         return upload_planes(FMT[fmt], w, scales, N, K)
     return upload_gguf(FMT[fmt], w, N, K)
 
@@ -27,7 +28,7 @@ def tiled_reference(fmt: str, codes_rows: np.ndarray, scales_rows: np.ndarray, N
     shorter); inside a tile, unit by unit, 16-byte part by part, the rows'
     parts side by side; scales the same way, one per unit and row."""
     E = 64 if fmt == "i8b64" else 32
-    P = {"q4_0": 1, "q8_0": 2, "i8b64": 4}[fmt]
+    P = {"q4_0": 1, "q8_0": 2, "i8b64": 4, "i8b32": 2}[fmt]
     nu = K // E
     out = np.zeros(lq.lq_packed_bytes(FMT[fmt], N, K), np.uint8)
     soff = lq.lq_scale_offset(FMT[fmt], N, K)

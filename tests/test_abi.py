@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 5
+    assert lq.lq_abi_version() == 6
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -53,9 +53,13 @@ def test_layout_sizes(L):
     assert lq.lq_packed_bytes(lq.LQ_I8B64, 5632, 2048) == _align256(5632 * 2048) + 4 * 5632 * 32
     assert lq.lq_gguf_bytes(lq.LQ_I8B64, 64, 64) == 0
     assert lq.lq_packed_bytes(lq.LQ_I8B64, 4, 96) == 0          # K not a multiple of 64
+    # the "oxinfer" page's Q8: 36 bytes per 32 weights (int8 codes + fp32 scale)
+    assert lq.lq_packed_bytes(lq.LQ_I8B32, 4096, 4096) == _align256(4096 * 4096) + 4096 * 4096 * 36 // 32 - 4096 * 4096
+    assert lq.lq_gguf_bytes(lq.LQ_I8B32, 64, 64) == 0
+    assert lq.lq_block_elems(lq.LQ_I8B32) == 32 and lq.lq_block_elems(4) == 0
     assert lq.lq_packed_bytes(7, 4, 64) == 0
     assert lq.lq_packed_bytes(lq.LQ_Q4_0, 0, 64) == 0
-    assert [lq.lq_block_elems(f) for f in (0, 1, 2, 3)] == [32, 32, 64, 0]
+    assert [lq.lq_block_elems(f) for f in (0, 1, 2, 3, 4)] == [32, 32, 64, 32, 0]
     # the packed bytes of a workload equal its GGUF bytes plus alignment padding
     assert lq.lq_packed_bytes(lq.LQ_Q4_0, 151936, 896) - lq.lq_gguf_bytes(lq.LQ_Q4_0, 151936, 896) < 256
 

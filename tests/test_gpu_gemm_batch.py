@@ -61,6 +61,8 @@ GROUPS = [
     ("i8b64", 33, [256, 65], 1024),
     ("i8b64", 512, [8200, 8264], 128),        # two 64-element units per row
     ("i8b64", 300, [64, 1000, 33, 4100], 192),  # four matrices, an odd number of units
+    ("i8b32", 512, [8200, 8264], 96),
+    ("i8b32", 33, [256, 65], 1024),
 ]
 
 

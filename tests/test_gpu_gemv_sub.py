@@ -41,6 +41,7 @@ SUB_SHAPES = [
     ("q8_0", 4000, 512),
     ("i8b64", 1, 64), ("i8b64", 15, 64), ("i8b64", 17, 8192), ("i8b64", 70, 640), ("i8b64", 130, 2048),
     ("i8b64", 4050, 1024),
+    ("i8b32", 1, 32), ("i8b32", 33, 4096), ("i8b32", 70, 640), ("i8b32", 4000, 512),
 ]
 
 
@@ -58,7 +59,8 @@ def test_sub_tile_parity(oracle, fmt, N, K, xdt):
     assert gu.ratio(y, yr, S, gu.GEMV_REL, gu.GEMV_ABS) <= 1.0
 
 
-@pytest.mark.parametrize("fmt,N,K", [("q8_0", 70, 1024), ("i8b64", 70, 1024), ("i8b64", 129, 256)])
+@pytest.mark.parametrize("fmt,N,K", [("q8_0", 70, 1024), ("i8b64", 70, 1024), ("i8b64", 129, 256),
+                                      ("i8b32", 70, 1024)])
 def test_sub_tile_one_hot_columns(fmt, N, K):
     say("gemv sub-tile one-hot", fmt, N, K)
     w, s = make(fmt, 5300 + N, N, K)

@@ -54,6 +54,8 @@ MULTI_SHAPES = [
     ("q8_0", 2, 130, 8192), ("q8_0", 1, 200, 5632), ("q8_0", 3, 3000, 2048), ("q8_0", 4, 77, 4096),
     ("q8_0", 4, 8200, 1024),
     ("i8b64", 2, 45, 5632), ("i8b64", 1, 130, 8192), ("i8b64", 3, 1500, 512), ("i8b64", 4, 300, 8192),
+    ("i8b32", 1, 3, 32), ("i8b32", 2, 70, 512), ("i8b32", 4, 130, 8192), ("i8b32", 7, 130, 2048),
+    ("i8b32", 16, 64, 8192), ("i8b32", 11, 200, 5632), ("i8b32", 16, 1100, 1024), ("i8b32", 3, 20000, 1024),
 ]
 
 
@@ -72,7 +74,7 @@ def test_multi_parity(oracle, fmt, M, N, K):
 
 
 @pytest.mark.parametrize("M", [16, 4, 2])
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64", "i8b32"])
 def test_multi_invariants(oracle, fmt, M):
     """Deterministic; doubling every scale doubles Y bit for bit; a one-hot
     token row gives the weight column exactly as lq_dequant_f32 unpacks it;
@@ -85,7 +87,7 @@ def test_multi_invariants(oracle, fmt, M):
     Y1 = gu.gemv_multi(fmt, Wd, X, M, N, K)
     Y2 = gu.gemv_multi(fmt, Wd, X, M, N, K)
     assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32)), "not deterministic"
-    if fmt == "i8b64":
+    if fmt in gu.PLANAR:
         w2, s2 = w, s * np.float32(2)
     else:
         bb = 18 if fmt == "q4_0" else 34
@@ -115,7 +117,8 @@ def test_multi_invariants(oracle, fmt, M):
 
 @pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 2, 151936 // 8, 896), ("q4_0", 2, 70, 25600),
                                         ("q8_0", 2, 8192, 2048), ("q8_0", 3, 130, 8192), ("q8_0", 4, 2048, 8192),
-                                        ("i8b64", 2, 300, 5632), ("i8b64", 3, 2048, 8192), ("i8b64", 4, 70, 8192)])
+                                        ("i8b64", 2, 300, 5632), ("i8b64", 3, 2048, 8192), ("i8b64", 4, 70, 8192),
+                                        ("i8b32", 3, 300, 4096), ("i8b32", 4, 20000, 1024)])
 def test_few_tokens_equal_single_token_rows(fmt, M, N, K):
     """A few tokens share each weight load, but every token row goes through
     the arithmetic of lq_gemv with fp16 activations on the same K split: the
@@ -133,10 +136,10 @@ def test_few_tokens_equal_single_token_rows(fmt, M, N, K):
 def test_multi_zero_codes():
     """Q4_0 codes all 8 and Q8_0 / int8 codes all 0 give exactly zero."""
     M, N, K = 9, 100, 2048
-    for fmt in ("q4_0", "q8_0", "i8b64"):
+    for fmt in ("q4_0", "q8_0", "i8b64", "i8b32"):
         say("gemv_multi zero codes", fmt)
         w, s = make(fmt, 5, N, K)
-        if fmt == "i8b64":
+        if fmt in gu.PLANAR:
             w = np.zeros_like(w)
         else:
             bb = 18 if fmt == "q4_0" else 34
@@ -154,7 +157,7 @@ def test_multi_batch_mixed(oracle):
     passes the oracle (the K split may differ between the two)."""
     cases = []
     for i in range(19):
-        fmt = ["q4_0", "q8_0", "i8b64"][i % 3]
+        fmt = ["q4_0", "q8_0", "i8b64", "i8b32"][i % 4]
         K = [64, 896, 2048, 5632][i % 4] if fmt != "i8b64" else [64, 2048, 5632][i % 3]
         N = 11 + 53 * i
         M = 1 + (5 * i) % 16

@@ -21,7 +21,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-ORACLE_FMT = {"q4_0": 0, "q8_0": 1, "i8b64": 2}
+ORACLE_FMT = {"q4_0": 0, "q8_0": 1, "i8b64": 2, "i8b32": 3}
 
 
 def say(*a):
@@ -42,12 +42,12 @@ def make(fmt, seed, N, K, c=None):
         return lqgen.q4_0_aos(seed, N, K, c or 0.02), None
     if fmt == "q8_0":
         return lqgen.q8_0_aos(seed, N, K, c or 0.005), None
-    return lqgen.i8b64_planes(seed, N, K, c or 0.003)
+    return lqgen.i8_planes(seed, N, K, 64 if fmt == "i8b64" else 32, c or 0.003)
 
 
 def set_scales(fmt, w, scales, N, K, values):
     """Overwrite the first scales of a generated matrix with special values."""
-    if fmt == "i8b64":
+    if fmt in gu.PLANAR:
         s = scales.copy()
         s[:len(values)] = np.array(values, np.float32)
         return w, s
@@ -64,7 +64,7 @@ def ref_dequant(o, fmt, w, scales, N, K):
 
 # ------------------------------------------------------------- dequant ----
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64", "i8b32"])
 def test_dequant_bitwise(oracle, fmt):
     N, K = 37, 448 if fmt != "i8b64" else 448
     say("dequant", fmt, N, K)
@@ -113,13 +113,14 @@ def test_dequant_golden_blocks(oracle):
 def test_repack_roundtrip_planes(N):
     """lq_repack_gguf and lq_pack_planes both produce the documented tiled
     layout, byte for byte, as built on the host from the same blocks."""
-    for fmt in ("q4_0", "q8_0", "i8b64"):
+    for fmt in ("q4_0", "q8_0", "i8b64", "i8b32"):
         K = 128 if fmt == "i8b64" else 224
         say("packed layout", fmt, N, K)
         w, s = make(fmt, 77 + N, N, K)
-        if fmt == "i8b64":
-            codes = w.reshape(N, K // 64, 64)
-            scales = s.reshape(N, K // 64)
+        if fmt in gu.PLANAR:
+            E = 64 if fmt == "i8b64" else 32
+            codes = w.reshape(N, K // E, E)
+            scales = s.reshape(N, K // E)
         else:
             bb = 18 if fmt == "q4_0" else 34
             blk = w.view(np.uint8).reshape(N, K // 32, bb)
@@ -129,7 +130,7 @@ def test_repack_roundtrip_planes(N):
         cb = N * K // 2 if fmt == "q4_0" else N * K
         off = lq.lq_scale_offset(gu.FMT[fmt], N, K)
         got = [("pack_planes", upload_planes(gu.FMT[fmt], codes.reshape(-1), scales.reshape(-1), N, K))]
-        if fmt != "i8b64":
+        if fmt not in gu.PLANAR:
             got.append(("repack_gguf", gu.upload(fmt, w, None, N, K)))
         for name, Wd in got:
             b = Wd.cpu().numpy()
@@ -148,6 +149,8 @@ GEMV_SHAPES = [
     ("q8_0", 6, 26624),
     ("i8b64", 1, 64), ("i8b64", 77, 128), ("i8b64", 256, 2048), ("i8b64", 45, 5632),
     ("i8b64", 12, 8192), ("i8b64", 5, 30720),
+    ("i8b32", 1, 32), ("i8b32", 77, 96), ("i8b32", 256, 2048), ("i8b32", 45, 5632), ("i8b32", 5, 30720),
+    ("i8b32", 20000, 1024),
 ]
 
 
@@ -169,8 +172,8 @@ def test_gemv_parity(oracle, fmt, N, K, xdt):
 def test_gemv_batch_mixed(oracle):
     """More than one launch group and more descriptors than one launch holds."""
     cases = []
-    for i in range(20):
-        fmt = ["q4_0", "q8_0", "i8b64"][i % 3]
+    for i in range(24):
+        fmt = ["q4_0", "q8_0", "i8b64", "i8b32"][i % 4]
         K = [64, 896, 2048, 5632][i % 4] if fmt != "i8b64" else [64, 2048, 5632][i % 3]
         N = 13 + 37 * i
         xdt = np.float16 if i % 2 else np.float32
@@ -246,7 +249,7 @@ def test_graph_replays_match_eager(oracle):
             assert torch.equal(o, e), f"eager run after replay {rep} differs"
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64", "i8b32"])
 def test_gemv_invariants(oracle, fmt):
     N, K = 96, 2048 if fmt != "q4_0" else 896
     say("gemv invariants", fmt, N, K)
@@ -257,7 +260,7 @@ def test_gemv_invariants(oracle, fmt):
     y2 = gu.gemv(fmt, Wd, x, N, K)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not deterministic"
     # every scale doubled -> y doubles bit for bit
-    if fmt == "i8b64":
+    if fmt in gu.PLANAR:
         w2, s2 = w, s * np.float32(2)
     else:
         bb = 18 if fmt == "q4_0" else 34
@@ -383,7 +386,7 @@ GEMM_INT8_SHAPES = [(16, 64, 64), (5, 33, 128), (130, 129, 256), (1, 128, 64), (
                     (512, 256, 1024), (64, 2048, 1408), (96, 200, 1152), (257, 385, 512)]
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q8_0", "i8b64", "i8b32"])
 @pytest.mark.parametrize("M,N,K", GEMM_INT8_SHAPES)
 def test_gemm_int8_formats(oracle, fmt, M, N, K):
     """Against the exact product at the GEMM bar, and tightly against the
@@ -401,7 +404,7 @@ def test_gemm_int8_formats(oracle, fmt, M, N, K):
     assert gu.ratio(Y, Yt, St, 1e-4, 1e-6) <= 1.0
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q8_0", "i8b64", "i8b32"])
 def test_gemm_int8_one_hot_rows(fmt):
     """X[m] = e_{k_m}: Q8_0 gives Y[m, :] = RN_fp16 of weight column k_m and
     int8 block-64 gives RN_fp32 of it (lq_dequant_f16 / lq_dequant_f32), bit
@@ -475,7 +478,7 @@ def test_matmul_routes_by_token_count():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("fmt", ["q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q8_0", "i8b64", "i8b32"])
 def test_workload_int8_prefill(oracle, fmt):
     """The prefill FFN shapes (2048 / 11008, M = 512) with int8 weights:
     sampled outputs against the exact product at the GEMM bar."""

@@ -61,7 +61,7 @@ def source(seed, N, K, sdt):
 SHAPES = [(1, 32), (6, 64), (65, 96), (130, 256), (7, 2048), (64, 896)]
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64", "i8b32"])
 @pytest.mark.parametrize("sdt", ["f32", "f16", "bf16"])
 def test_quantize_bitwise(oracle, fmt, sdt):
     for N, K in SHAPES:
@@ -87,7 +87,7 @@ def test_quantize_then_gemv(oracle):
     """fp32 weights quantized on the GPU and multiplied there agree with the
     oracle's GEMV over the oracle's quantization of the same weights."""
     N, K = 300, 2048
-    for fmt in ("q4_0", "q8_0", "i8b64"):
+    for fmt in ("q4_0", "q8_0", "i8b64", "i8b32"):
         say("quantize + gemv", fmt, N, K)
         w = (lqgen.activations(77, N * K, np.float32) * 0.02).reshape(N, K)
         Wd = empty_packed(gu.FMT[fmt], N, K)

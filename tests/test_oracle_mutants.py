@@ -23,8 +23,8 @@ MUTANTS = {
     # scale bytes read big-endian
     "scale_endianness": ("const double d = half_to_double(static_cast<uint16_t>(b[0] | (b[1] << 8)));\n    for (int j = 0; j < 16; ++j)",
                          "const double d = half_to_double(static_cast<uint16_t>((b[0] << 8) | b[1]));\n    for (int j = 0; j < 16; ++j)"),
-    # int8 block-64 scale index using 32-wide blocks
-    "i8_scale_index": ("static_cast<double>(s[k / 64])", "static_cast<double>(s[k / 32 % (K / 64)])"),
+    # int8 scale index using 32-wide blocks whatever the block size
+    "i8_scale_index": ("static_cast<double>(s[k / E])", "static_cast<double>(s[k / 32 % (K / E)])"),
     # S without the absolute value
     "abs_dropped": ("abs_acc += std::fabs(p);\n        }\n        y[i] = acc;", "abs_acc += p;\n        }\n        y[i] = acc;"),
     # GEMM reads X transposed

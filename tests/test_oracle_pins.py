@@ -23,7 +23,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-Q4_0, Q8_0, I8B64 = 0, 1, 2
+Q4_0, Q8_0, I8B64, I8B32 = 0, 1, 2, 3
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "blocks.json")))
 
 
@@ -220,6 +220,39 @@ def pin_cross_format(o):
                           o.dequant(Q8_0, q8b, None, N, K))
 
 
+def pin_i8b32_against_other_formats(o):
+    """The "oxinfer" page's Q8 (int8 codes, one fp32 scale per 32) pinned to
+    the independently pinned formats: with each 64-block's scale repeated
+    for both of its halves it is I8B64 exactly; with fp16-representable
+    scales it is Q8_0 exactly (dequant and GEMV); its quantizer on a
+    32-block h equals the I8B64 quantizer on the 64-block [h, h]."""
+    rng = np.random.default_rng(23)
+    N, K = 5, 128
+    c = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    s64 = (np.abs(rng.standard_normal(N * K // 64)) * 0.01).astype(np.float32)
+    s32 = np.repeat(s64, 2)
+    assert np.array_equal(o.dequant(I8B32, c.reshape(-1), s32, N, K), o.dequant(I8B64, c.reshape(-1), s64, N, K))
+    s16 = (np.abs(rng.standard_normal(N * K // 32)) * 0.01).astype(np.float16)
+    q8 = []
+    for n in range(N):
+        for b in range(K // 32):
+            q8 += _q8_block_bytes(c[n, b * 32:(b + 1) * 32], int(s16[n * (K // 32) + b].view(np.uint16)))
+    q8 = np.array(q8, np.uint8)
+    assert np.array_equal(o.dequant(I8B32, c.reshape(-1), s16.astype(np.float32), N, K),
+                          o.dequant(Q8_0, q8, None, N, K))
+    x = rng.standard_normal(K).astype(np.float32)
+    assert np.array_equal(o.gemv(I8B32, c.reshape(-1), s16.astype(np.float32), x, N, K)[0],
+                          o.gemv(Q8_0, q8, None, x, N, K)[0])
+    w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    q32, sc32 = o.quantize(I8B32, w, N, K)
+    dup = np.concatenate([np.repeat(w.reshape(N, K // 32, 1, 32), 2, axis=2)], axis=0).reshape(N, 2 * K)
+    q64, sc64 = o.quantize(I8B64, dup, N, 2 * K)
+    q64 = q64.reshape(N, K // 32, 2, 32)
+    assert np.array_equal(q32.reshape(N, K // 32, 32), q64[:, :, 0, :])
+    assert np.array_equal(q64[:, :, 0, :], q64[:, :, 1, :])
+    assert np.array_equal(sc32.view(np.uint32), sc64.view(np.uint32))
+
+
 def pin_scale_linearity_and_gemm(o):
     rng = np.random.default_rng(9)
     N, K, M = 6, 64, 5
@@ -279,6 +312,7 @@ def pin_byte_accounting(o):
     assert o.block_elems(Q4_0) == 32 and o.gguf_block_bytes(Q4_0) == 18
     assert o.block_elems(Q8_0) == 32 and o.gguf_block_bytes(Q8_0) == 34
     assert o.block_elems(I8B64) == 64
+    assert o.block_elems(I8B32) == 32 and o.gguf_block_bytes(I8B32) == 0
     assert round(2.0 / (18 / 32), 1) in (3.5, 3.6)
     assert round(2.0 / (36 / 32), 1) == 1.8
 
@@ -292,7 +326,7 @@ def pin_argument_checks(o):
 
 ALL_PINS = [pin_half_decode, pin_half_encode, pin_golden_blocks, pin_i8b64_single_rounding,
             pin_bruteforce, pin_closed_forms, pin_cross_format, pin_scale_linearity_and_gemm,
-            pin_roundtrip, pin_byte_accounting, pin_argument_checks]
+            pin_roundtrip, pin_byte_accounting, pin_argument_checks, pin_i8b32_against_other_formats]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
