@@ -334,7 +334,8 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
 extern "C" {
 
 static_assert(LQ_GEMM_MAX_GROUP == lq::kMaxGemmGroup, "GEMM group size");
-static_assert(LQ_Q4_0 == lq::kQ4_0 && LQ_Q8_0 == lq::kQ8_0 && LQ_I8B64 == lq::kI8B64 && LQ_I8B32 == lq::kI8B32,
+static_assert(int(LQ_Q4_0) == int(lq::kQ4_0) && int(LQ_Q8_0) == int(lq::kQ8_0) &&
+                  int(LQ_I8B64) == int(lq::kI8B64) && int(LQ_I8B32) == int(lq::kI8B32),
               "format numbering");
 
 int32_t lq_abi_version(void) { return LQ_ABI_VERSION; }
