@@ -105,7 +105,7 @@ def x_max_k():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "i8b64", "i8b32"])
 def test_max_k_full_tile(oracle, fmt, x_max_k):
     """K at the documented maximum (2^25) with a full 64-row tile: the 32-bit
     offsets inside a tile reach their largest values.  Weights are generated
