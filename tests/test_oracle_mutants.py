@@ -31,6 +31,9 @@ MUTANTS = {
     "gemm_transposed_x": ("x_at(X, xdt, ms[a] * K + k)", "x_at(X, xdt, k * M + ms[a])"),
     # fp16 encoder rounds ties up instead of to even
     "ties_up": ("return (std::fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    # fp16 tile of the fp32-scale formats rounded through fp32 first (double rounding)
+    "f16_via_f32": ("for (int64_t k = 0; k < K; ++k) out[n * K + k] = double_to_half(row[k]);",
+                    "for (int64_t k = 0; k < K; ++k) out[n * K + k] = double_to_half(static_cast<float>(row[k]));"),
     # GEMM ignores the fp16 tile rounding flag
     "gemm_no_f16_round": ("if (round_w_f16)", "if (false && round_w_f16)"),
     # quantizer: ties rounded away from zero instead of to even

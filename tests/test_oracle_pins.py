@@ -102,6 +102,71 @@ def pin_i8b64_single_rounding(o):
     assert d[0] == -32.0 and d[63] == -0.5 and d[64] == 0.0 and d[127] == 63 * 0.25
 
 
+def _half_of_exact(c, s):
+    """numpy's direct double -> binary16 cast (round to nearest even, one
+    rounding) of the exact product c * s."""
+    with np.errstate(over="ignore"):
+        return (np.asarray(c, np.float64) * np.asarray(s, np.float32).astype(np.float64)).astype(np.float16).view(np.uint16)
+
+
+def _double_rounding_cases():
+    """(code, fp32 scale) pairs whose exact product lies just off an fp16
+    halfway point, inside half an fp32 ulp of it: rounding the product to
+    fp32 first lands on the halfway point and then ties to even, which is
+    not RN_fp16 of the exact product.  Found by search, checked here."""
+    rng = np.random.default_rng(2024)
+    cases = []
+    for h in rng.integers(0x0001, 0x7BFE, 300).astype(np.uint16):
+        lo, hi = np.array([h, h + 1], np.uint16).view(np.float16).astype(np.float64)
+        t = (lo + hi) / 2
+        for c in (3, 5, 7, 11, 13, 127, -3, -9, -117):
+            s0 = np.float32(t / c)
+            for s in (np.nextafter(s0, np.float32(-np.inf)), s0, np.nextafter(s0, np.float32(np.inf))):
+                p = float(c) * float(s)
+                via32 = np.array([np.float32(p)], np.float32).astype(np.float16).view(np.uint16)[0]
+                if _half_of_exact(c, s) != via32:
+                    cases.append((c, s))
+    assert len(cases) > 100
+    return cases
+
+
+def pin_int8_f16_single_rounding(o):
+    """dequant_f16 of the fp32-scale formats is RN_fp16 of the exact product
+    c * s, rounded once from the exact value (numpy's double -> half cast):
+    random codes and scales in the generated ranges and above, products
+    that a rounding through fp32 would move (double rounding), exact ties,
+    fp16 subnormals and overflow to inf."""
+    rng = np.random.default_rng(77)
+    pairs = _double_rounding_cases()
+    # exact halfway points between fp16 neighbours, as c * s with c = +-1, +-2
+    h = rng.integers(0x0001, 0x7BFE, 200).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    for c, m in ((1, (lo + hi) / 2), (-2, (lo + hi) / 4)):
+        pairs += [(c, np.float32(v)) for v in m if float(np.float32(v)) == v]
+    # subnormal results (and their halfway points), the largest finite value
+    # and the overflow boundary 65520
+    pairs += [(1, np.float32(2.0 ** -25)), (3, np.float32(2.0 ** -25)), (5, np.float32(2.0 ** -26)),
+              (1, np.float32(2.0 ** -24 * 1.5)), (-1, np.float32(2.0 ** -24 * 2.5)), (7, np.float32(1e-9)),
+              (127, np.float32(65504.0 / 127)), (1, np.float32(65504.0)), (1, np.float32(65519.0)),
+              (2, np.float32(32760.0)), (-2, np.float32(32760.0)), (127, np.float32(600.0)),
+              (1, np.float32(65520.0)), (0, np.float32(3.0)), (-128, np.float32(0.5))]
+    for fmt, E in ((I8B64, 64), (I8B32, 32)):
+        # one code and one scale per block: the tested pair sits at element 0
+        # of its block, the rest of the block are random codes
+        nb = len(pairs)
+        K = E * 4
+        N = (nb + 3) // 4
+        codes = rng.integers(-127, 128, N * K).astype(np.int8)
+        scales = (np.abs(rng.standard_normal(N * 4)) * rng.choice([0.003, 0.5, 20.0], N * 4)).astype(np.float32)
+        for i, (c, s) in enumerate(pairs):
+            codes[i * E] = c
+            scales[i] = s
+        got = o.dequant_f16(fmt, codes, scales, N, K).reshape(-1)
+        want = _half_of_exact(codes.astype(np.float64), np.repeat(scales, E))
+        assert np.array_equal(got, want), fmt
+
+
 # ----------------------------------------------------------------- brute force
 
 def _q4_block_bytes(codes32, dbits):
@@ -326,7 +391,8 @@ def pin_argument_checks(o):
 
 ALL_PINS = [pin_half_decode, pin_half_encode, pin_golden_blocks, pin_i8b64_single_rounding,
             pin_bruteforce, pin_closed_forms, pin_cross_format, pin_scale_linearity_and_gemm,
-            pin_roundtrip, pin_byte_accounting, pin_argument_checks, pin_i8b32_against_other_formats]
+            pin_roundtrip, pin_byte_accounting, pin_argument_checks, pin_i8b32_against_other_formats,
+            pin_int8_f16_single_rounding]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
