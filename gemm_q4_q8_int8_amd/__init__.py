@@ -22,8 +22,8 @@ FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64, "i8b32": LQ_I8B3
 # Every symbol include/lq.h declares.
 EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq_scale_offset",
            "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_quantize", "lq_dequant_f32",
-           "lq_dequant_f16", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi", "lq_gemv_multi_batch",
-           "lq_gemm_workspace_bytes",
+           "lq_dequant_f16", "lq_gemv_workspace_bytes", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi",
+           "lq_gemv_multi_batch", "lq_gemm_workspace_bytes",
            "lq_gemm", "lq_gemm_batch",
            "lq_matmul", "lq_status_str", "lq_last_error")
 
@@ -82,10 +82,11 @@ def load(path: str = LIB_PATH):
         "lq_quantize": ([i32, vp, i32, vp, i64, i64, vp], i32),
         "lq_dequant_f32": ([i32, vp, vp, i64, i64, vp], i32),
         "lq_dequant_f16": ([i32, vp, vp, i64, i64, vp], i32),
-        "lq_gemv": ([i32, vp, vp, i32, vp, i64, i64, vp], i32),
-        "lq_gemv_batch": ([ctypes.POINTER(lq_gemv_desc), i32, vp], i32),
-        "lq_gemv_multi": ([i32, vp, vp, i32, vp, i64, i64, i64, vp], i32),
-        "lq_gemv_multi_batch": ([ctypes.POINTER(lq_gemv_multi_desc), i32, vp], i32),
+        "lq_gemv_workspace_bytes": ([], sz),
+        "lq_gemv": ([i32, vp, vp, i32, vp, i64, i64, vp, sz, vp], i32),
+        "lq_gemv_batch": ([ctypes.POINTER(lq_gemv_desc), i32, vp, sz, vp], i32),
+        "lq_gemv_multi": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
+        "lq_gemv_multi_batch": ([ctypes.POINTER(lq_gemv_multi_desc), i32, vp, sz, vp], i32),
         "lq_gemm_workspace_bytes": ([i32, i64, i64, i64], sz),
         "lq_gemm": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_gemm_batch": ([i32, vp, i32, i64, i64, ctypes.POINTER(lq_gemm_desc), i32, vp, sz, vp], i32),
@@ -114,6 +115,15 @@ def _ptr(t):
     if isinstance(t, int):
         return t
     return t.data_ptr()
+
+
+def _ws_bytes(ws, ws_bytes):
+    """Workspace size: as given, else the whole tensor (0 without one)."""
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    if ws is None or isinstance(ws, int):
+        return 0
+    return ws.numel() * ws.element_size()
 
 
 def _stream(stream):
@@ -164,6 +174,10 @@ def lq_gguf_bytes(fmt, N, K) -> int:
     return load().lq_gguf_bytes(_fmt(fmt), N, K)
 
 
+def lq_gemv_workspace_bytes() -> int:
+    return load().lq_gemv_workspace_bytes()
+
+
 def lq_gemm_workspace_bytes(fmt, M, N, K) -> int:
     return load().lq_gemm_workspace_bytes(_fmt(fmt), M, N, K)
 
@@ -203,50 +217,53 @@ def lq_dequant_f16(fmt, W, out, N, K, stream=None):
     _check(load().lq_dequant_f16(_fmt(fmt), _ptr(W), _ptr(out), N, K, _stream(stream)))
 
 
-def lq_gemv(fmt, W, x, y, N, K, stream=None, xdt=None):
+def lq_gemv(fmt, W, x, y, N, K, ws=None, ws_bytes=None, stream=None, xdt=None):
+    """ws: optional GEMV workspace (lq_gemv_workspace_bytes() bytes)."""
     xdt = _xdt(x) if xdt is None else xdt
-    _check(load().lq_gemv(_fmt(fmt), _ptr(W), _ptr(x), xdt, _ptr(y), N, K, _stream(stream)))
+    _check(load().lq_gemv(_fmt(fmt), _ptr(W), _ptr(x), xdt, _ptr(y), N, K, _ptr(ws),
+                          _ws_bytes(ws, ws_bytes), _stream(stream)))
 
 
-def lq_gemv_batch(descs, stream=None):
+def lq_gemv_batch(descs, ws=None, ws_bytes=None, stream=None):
     """descs: sequence of (fmt, W, x, y, N, K) tuples of tensors / sizes."""
     arr = (lq_gemv_desc * max(1, len(descs)))()
     for i, (fmt, W, x, y, N, K) in enumerate(descs):
         arr[i] = lq_gemv_desc(_fmt(fmt), _xdt(x), _ptr(W), _ptr(x), _ptr(y), N, K)
-    _check(load().lq_gemv_batch(arr, len(descs), _stream(stream)))
+    _check(load().lq_gemv_batch(arr, len(descs), _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)))
 
 
-def lq_gemv_multi(fmt, W, X, Y, M, N, K, stream=None, xdt=None):
+def lq_gemv_multi(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=None, stream=None, xdt=None):
     xdt = _xdt(X) if xdt is None else xdt
-    _check(load().lq_gemv_multi(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K,
-                                _stream(stream)))
+    _check(load().lq_gemv_multi(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K, _ptr(ws),
+                                _ws_bytes(ws, ws_bytes), _stream(stream)))
 
 
-def lq_gemv_multi_batch(descs, stream=None):
+def lq_gemv_multi_batch(descs, ws=None, ws_bytes=None, stream=None):
     """descs: sequence of (fmt, W, X, Y, M, N, K) tuples of tensors / sizes."""
     arr = (lq_gemv_multi_desc * max(1, len(descs)))()
     for i, (fmt, W, X, Y, M, N, K) in enumerate(descs):
         arr[i] = lq_gemv_multi_desc(_fmt(fmt), _xdt(X), _ptr(W), _ptr(X), _ptr(Y), M, N, K)
-    _check(load().lq_gemv_multi_batch(arr, len(descs), _stream(stream)))
+    _check(load().lq_gemv_multi_batch(arr, len(descs), _ptr(ws), _ws_bytes(ws, ws_bytes),
+                                      _stream(stream)))
 
 
-def lq_gemm(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=0, stream=None, xdt=None):
+def lq_gemm(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=None, stream=None, xdt=None):
     xdt = _xdt(X) if xdt is None else xdt
-    _check(load().lq_gemm(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K, _ptr(ws), ws_bytes,
-                          _stream(stream)))
+    _check(load().lq_gemm(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K, _ptr(ws),
+                          _ws_bytes(ws, ws_bytes), _stream(stream)))
 
 
-def lq_gemm_batch(fmt, X, M, K, descs, ws=None, ws_bytes=0, stream=None, xdt=None):
+def lq_gemm_batch(fmt, X, M, K, descs, ws=None, ws_bytes=None, stream=None, xdt=None):
     """descs: sequence of (W, Y, N): weight matrices sharing X, M and K."""
     xdt = _xdt(X) if xdt is None else xdt
     arr = (lq_gemm_desc * max(1, len(descs)))()
     for i, (W, Y, N) in enumerate(descs):
         arr[i] = lq_gemm_desc(_ptr(W), _ptr(Y), N)
-    _check(load().lq_gemm_batch(_fmt(fmt), _ptr(X), xdt, M, K, arr, len(descs), _ptr(ws), ws_bytes,
-                                _stream(stream)))
+    _check(load().lq_gemm_batch(_fmt(fmt), _ptr(X), xdt, M, K, arr, len(descs), _ptr(ws),
+                                _ws_bytes(ws, ws_bytes), _stream(stream)))
 
 
-def lq_matmul(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=0, stream=None, xdt=None):
+def lq_matmul(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=None, stream=None, xdt=None):
     xdt = _xdt(X) if xdt is None else xdt
-    _check(load().lq_matmul(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K, _ptr(ws), ws_bytes,
-                            _stream(stream)))
+    _check(load().lq_matmul(_fmt(fmt), _ptr(W), _ptr(X), xdt, _ptr(Y), M, N, K, _ptr(ws),
+                            _ws_bytes(ws, ws_bytes), _stream(stream)))

@@ -24,7 +24,7 @@ ARCH = os.environ.get("LQ_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wall", "-Wno-unused-command-line-argument"]
+          "-Wall", "-Werror", "-Wno-unused-command-line-argument"]
 
 
 # Per-source extra flags.  The multi-token GEMV takes its MFMA results in

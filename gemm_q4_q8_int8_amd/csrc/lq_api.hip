@@ -5,6 +5,7 @@
 #include "lq_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -82,6 +83,20 @@ lq_status device_cus(int* cus) {
     return LQ_OK;
 }
 
+// A GEMV workspace is optional; when given it must hold
+// lq_gemv_workspace_bytes() bytes and be 16-byte aligned.
+lq_status check_gemv_ws(const void* ws, size_t ws_bytes) {
+    if (!ws) return LQ_OK;
+    if (ws_bytes < lq::kGemvWorkspaceBytes)
+        return fail(LQ_ERR_WORKSPACE, "GEMV workspace of %zu bytes required, %zu given", lq::kGemvWorkspaceBytes,
+                    ws_bytes);
+    if (!aligned(ws, 16)) return fail(LQ_ERR_ALIGN, "ws is not 16-byte aligned");
+    return LQ_OK;
+}
+
+// Most tokens lq_matmul sends to the multi-token GEMV; more go to the GEMM.
+constexpr int64_t kMatmulGemvMaxTokens = lq::kMultiMaxTokens;
+
 lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
     lq_status st = check_fmt_shape(d.fmt, d.N, d.K);
     if (st != LQ_OK) return st;
@@ -100,8 +115,9 @@ lq_status check_gemv_desc(const lq_gemv_desc& d, int idx) {
 // its workgroups get about the same number of units (the launch's total work
 // spread over that many workgroups), never below min_units per wave (per
 // format: gemv_min_units, multi_min_units).  Equal work per workgroup keeps
-// a long-K matrix from becoming the tail of the launch.  M[i] tokens of partials per row count against the
-// split-K scratch; if it does not fit, nothing is split.
+// a long-K matrix from becoming the tail of the launch.  M[i] tokens of
+// partials per row count against the split-K workspace; if they do not fit,
+// nothing is split.
 void split_k(int min_units, int cus, const std::vector<int64_t>& tiles, const std::vector<int64_t>& nu,
              const std::vector<int64_t>& M, std::vector<int64_t>& S) {
     const size_t n = tiles.size();
@@ -118,7 +134,7 @@ void split_k(int min_units, int cus, const std::vector<int64_t>& tiles, const st
     for (size_t i = 0; i < n; ++i) {
         const int64_t cap = std::max<int64_t>(1, nu[i] / (4 * min_units));
         const int64_t want = std::max<int64_t>(1, int64_t(double(nu[i]) / per_wg + 0.5));
-        S[i] = std::min(want, cap);
+        S[i] = std::min(std::min(want, cap), lq::kMaxSlices);
         if (S[i] > 1) {
             part += S[i] * M[i] * tiles[i] * lq::kTileRows;
             cnt += tiles[i];
@@ -150,10 +166,23 @@ struct GemvJob {
     int64_t K;
 };
 
+// Workspace of a GEMV call: the counters, then the partial sums (NULL when
+// the caller gave none: then no launch splits K across workgroups).
+struct GemvWs {
+    uint64_t* cnt;
+    float* part;
+};
+GemvWs gemv_ws(void* ws) {
+    if (!ws) return {nullptr, nullptr};
+    uint64_t* c = static_cast<uint64_t*>(ws);
+    return {c, reinterpret_cast<float*>(c + lq::kGemvCounters)};
+}
+
 // One grouped GEMV launch: up to kMaxBatch matrices of one format and
-// activation dtype, each over mt tokens (1, or 2 with fp16 activations), K
-// split by split_k.
-lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, int cus, hipStream_t stream) {
+// activation dtype, each over mt tokens (1 .. gemv_max_tokens with fp16
+// activations), K split by split_k when a workspace is given.
+lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, int cus, GemvWs ws,
+                       hipStream_t stream) {
     const int n = int(g.size());
     std::vector<int64_t> tiles(n), nu(n), S(n, 1);
     for (int i = 0; i < n; ++i) {
@@ -211,14 +240,11 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
         waves = 16;
         for (int i = 0; i < n; ++i) S[i] = (S[i] + 3) / 4;
     }
-    float* part = nullptr;
-    uint32_t* cntp = nullptr;
-    bool any_split = false;
-    for (int i = 0; i < n; ++i) any_split = any_split || S[i] > 1;
-    if (any_split) {
-        const hipError_t e = lq::gemv_scratch(&part, &cntp);
-        if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
-    }
+    // Without a workspace the K slices of a tile stay inside its workgroup.
+    if (!ws.cnt)
+        for (int i = 0; i < n; ++i) S[i] = 1;
+    float* part = ws.part;
+    uint64_t* cntp = ws.cnt;
     const std::vector<int> ord = split_first(S);
     lq::GemvArgs a = {};
     int64_t wgs = 0, part_off = 0, cnt_off = 0;
@@ -247,6 +273,7 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
         wgs += tiles[i] * S[i];
         if (wgs > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
     }
+    a.tag = lq::next_splitk_tag();
     a.count = n;
     a.total_wgs = int32_t(wgs);
     const hipError_t e = lq::launch_gemv(fmt, xdt, waves, mt, a, stream);
@@ -273,8 +300,8 @@ lq_status check_multi_desc(const lq_gemv_multi_desc& d, int idx) {
 
 // One grouped multi-token launch: up to kMaxBatch descriptors of one format.
 // The K split follows the single-token rule, with the partials of M tokens
-// per row counted against the scratch area.
-lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc*>& g, int cus,
+// per row counted against the workspace (no split without one).
+lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc*>& g, int cus, GemvWs ws,
                              hipStream_t stream) {
     const int n = int(g.size());
     std::vector<int64_t> tiles(n), nu(n), S(n, 1);
@@ -285,14 +312,10 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
     std::vector<int64_t> Ms(n);
     for (int i = 0; i < n; ++i) Ms[i] = g[i]->M;
     split_k(lq::multi_min_units(fmt), cus, tiles, nu, Ms, S);
-    float* part = nullptr;
-    uint32_t* cntp = nullptr;
-    bool any_split = false;
-    for (int i = 0; i < n; ++i) any_split = any_split || S[i] > 1;
-    if (any_split) {
-        const hipError_t e = lq::gemv_scratch(&part, &cntp);
-        if (e != hipSuccess) return hip_fail(e, "GEMV scratch lookup");
-    }
+    if (!ws.cnt)
+        for (int i = 0; i < n; ++i) S[i] = 1;
+    float* part = ws.part;
+    uint64_t* cntp = ws.cnt;
     const std::vector<int> ord = split_first(S);
     lq::MultiArgs a = {};
     int64_t wgs = 0, part_off = 0, cnt_off = 0;
@@ -323,6 +346,7 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
         wgs += tiles[i] * S[i];
         if (wgs > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
     }
+    a.tag = lq::next_splitk_tag();
     a.count = n;
     a.total_wgs = int32_t(wgs);
     const hipError_t e = lq::launch_gemv_multi(fmt, a, stream);
@@ -330,6 +354,15 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
 }
 
 }  // namespace
+
+namespace lq {
+// Tags count up from 1 in the low 48 bits (the counter word keeps 16 bits
+// for arrivals): 2^48 launches never wrap in a process's lifetime.
+uint64_t next_splitk_tag() {
+    static std::atomic<uint64_t> next{1};
+    return next.fetch_add(1, std::memory_order_relaxed) & ((uint64_t(1) << 48) - 1);
+}
+}  // namespace lq
 
 extern "C" {
 
@@ -414,14 +447,20 @@ lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out, int64_t N, i
     return dequant_common(fmt, W, out, N, K, stream, true);
 }
 
-lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream) {
+size_t lq_gemv_workspace_bytes(void) { return lq::kGemvWorkspaceBytes; }
+
+lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* ws, size_t ws_bytes, void* stream) {
     if (!descs) return fail(LQ_ERR_ARG, "descs is NULL");
     if (count < 1) return fail(LQ_ERR_ARG, "count=%d must be >= 1", count);
     for (int32_t i = 0; i < count; ++i) LQ_TRY(check_gemv_desc(descs[i], i));
+    LQ_TRY(check_gemv_ws(ws, ws_bytes));
     int cus = 0;
     LQ_TRY(device_cus(&cus));
+    const GemvWs w = gemv_ws(ws);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
     // Group descriptors that share a kernel (format and activation dtype),
     // keeping their order, and launch each group in chunks of kMaxBatch.
+    // Launches on one stream run in order, so they share the workspace.
     std::vector<bool> done(size_t(count), false);
     for (int32_t i = 0; i < count; ++i) {
         if (done[i]) continue;
@@ -431,18 +470,17 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream) 
             chunk.push_back({descs[j].W, descs[j].x, descs[j].y, descs[j].N, descs[j].K});
             done[j] = true;
             if (chunk.size() == size_t(lq::kMaxBatch)) {
-                LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, static_cast<hipStream_t>(stream)));
+                LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, w, st));
                 chunk.clear();
             }
         }
-        if (!chunk.empty())
-            LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, static_cast<hipStream_t>(stream)));
+        if (!chunk.empty()) LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, w, st));
     }
     return LQ_OK;
 }
 
 lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt, float* y, int64_t N,
-                  int64_t K, void* stream) {
+                  int64_t K, void* ws, size_t ws_bytes, void* stream) {
     lq_gemv_desc d;
     d.fmt = fmt;
     d.xdt = xdt;
@@ -451,15 +489,18 @@ lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt, float*
     d.y = y;
     d.N = N;
     d.K = K;
-    return lq_gemv_batch(&d, 1, stream);
+    return lq_gemv_batch(&d, 1, ws, ws_bytes, stream);
 }
 
-lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* stream) {
+lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* ws, size_t ws_bytes,
+                              void* stream) {
     if (!descs) return fail(LQ_ERR_ARG, "descs is NULL");
     if (count < 1) return fail(LQ_ERR_ARG, "count=%d must be >= 1", count);
     for (int32_t i = 0; i < count; ++i) LQ_TRY(check_multi_desc(descs[i], i));
+    LQ_TRY(check_gemv_ws(ws, ws_bytes));
     int cus = 0;
     LQ_TRY(device_cus(&cus));
+    const GemvWs w = gemv_ws(ws);
     // Group by format and kernel, keeping order, in chunks of kMaxBatch.  Up
     // to lq::gemv_max_tokens(fmt) tokens run on the single-token GEMV kernel
     // (a few fp16 dot products per weight on the vector units, still under
@@ -481,22 +522,22 @@ lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, vo
             if (kern == 0) chunk.push_back(&descs[j]);
             else jobs.push_back({descs[j].W, descs[j].X, descs[j].Y, descs[j].N, descs[j].K});
             if (chunk.size() == size_t(lq::kMaxBatch)) {
-                LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, st));
+                LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, w, st));
                 chunk.clear();
             }
             if (jobs.size() == size_t(lq::kMaxBatch)) {
-                LQ_TRY(launch_chunk(descs[i].fmt, LQ_F16, int(kern), jobs, cus, st));
+                LQ_TRY(launch_chunk(descs[i].fmt, LQ_F16, int(kern), jobs, cus, w, st));
                 jobs.clear();
             }
         }
-        if (!chunk.empty()) LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, st));
-        if (!jobs.empty()) LQ_TRY(launch_chunk(descs[i].fmt, LQ_F16, int(kern), jobs, cus, st));
+        if (!chunk.empty()) LQ_TRY(launch_multi_chunk(descs[i].fmt, chunk, cus, w, st));
+        if (!jobs.empty()) LQ_TRY(launch_chunk(descs[i].fmt, LQ_F16, int(kern), jobs, cus, w, st));
     }
     return LQ_OK;
 }
 
 lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
-                        int64_t N, int64_t K, void* stream) {
+                        int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
     lq_gemv_multi_desc d;
     d.fmt = fmt;
     d.xdt = xdt;
@@ -506,7 +547,7 @@ lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, 
     d.M = M;
     d.N = N;
     d.K = K;
-    return lq_gemv_multi_batch(&d, 1, stream);
+    return lq_gemv_multi_batch(&d, 1, ws, ws_bytes, stream);
 }
 
 namespace {
@@ -565,9 +606,14 @@ lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int6
 
 lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt, float* Y, int64_t M,
                     int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
-    if (M == 1) return lq_gemv(fmt, W, X, xdt, Y, N, K, stream);
-    if (M <= lq::kMultiMaxTokens && xdt == LQ_F16)
-        return lq_gemv_multi(fmt, W, X, xdt, Y, M, N, K, stream);
+    // The GEMV paths take ws as their split-K workspace when it is large
+    // enough for one, else run without.
+    const bool gemv_ws_ok = ws && ws_bytes >= lq::kGemvWorkspaceBytes && aligned(ws, 16);
+    void* gws = gemv_ws_ok ? ws : nullptr;
+    const size_t gwb = gemv_ws_ok ? ws_bytes : 0;
+    if (M == 1) return lq_gemv(fmt, W, X, xdt, Y, N, K, gws, gwb, stream);
+    if (M <= kMatmulGemvMaxTokens && xdt == LQ_F16)
+        return lq_gemv_multi(fmt, W, X, xdt, Y, M, N, K, gws, gwb, stream);
     return lq_gemm(fmt, W, X, xdt, Y, M, N, K, ws, ws_bytes, stream);
 }
 

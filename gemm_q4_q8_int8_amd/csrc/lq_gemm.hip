@@ -193,12 +193,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
     //      into the tile); then NT scale loads; the rest a spare load of
     //      scales into the slot's dummy area (keeps the per-wave count
     //      uniform for the wait).
-    uint32_t xo[2];
+    // Byte offsets into X are 64-bit: X may exceed 4 GiB (M K 2 bytes).
+    size_t xo[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = 32 * wave + 16 * i + (lane >> 2);
         const int c = (lane & 3) ^ ((row >> 2) & 3);
-        xo[i] = uint32_t(min(m0 + row, a.M - 1)) * uint32_t(a.K) * 2u + uint32_t(c) * 16u;
+        xo[i] = size_t(min(m0 + row, a.M - 1)) * size_t(a.K) * 2u + size_t(c) * 16u;
     }
     constexpr int kOthers = C::kOthers;
     const uint8_t* osrc[kOthers];   // per-lane source of the step-0 block

@@ -17,14 +17,14 @@
 //     LDS in a fixed order.  When the matrices
 //     of a launch have too few tiles to fill the chip (one 2048-row matrix is
 //     32 tiles), K is also split across S workgroups per tile: each writes
-//     its slice's sums to a per-device scratch area and bumps the tile's
+//     its slice's sums to the caller's workspace and bumps the tile's
 //     arrival counter; the last one to arrive adds the S slices in slice
 //     order (deterministic) and writes y.
 //   * Each wave issues the loads of a batch of UNR units before it computes
 //     any of them (all in flight at once, consumed in load order).  UNR is
 //     chosen per launch so that the batches split a wave's units evenly: a
-//     slot past the wave's last unit still loads and computes (its sum is
-//     masked off), since per-slot branches let the compiler sink loads below
+//     slot past the wave's last unit still loads and computes (a select then
+//     leaves the sums unchanged), since per-slot branches let the compiler sink loads below
 //     the first slot's arithmetic.  Q4_0 (most arithmetic per byte) takes
 //     up to 8 units per batch, Q8_0 2 and int8 block-64 1 (2 in launches with
 //     few waves): with the waves resident per SIMD, larger batches were
@@ -38,20 +38,11 @@
 //     fp32 FMA (fp32 activations), or a byte permute into fp16 pairs and
 //     v_dot2 (fp16 activations).
 //   * The block scale multiplies the unit's partial sum once per block.
-#include "lq_internal.h"
+#include "lq_splitk.h"
 
-#include <mutex>
 #include <type_traits>
 
 namespace lq {
-
-// Split-K scratch of this device: partial sums and per-tile arrival counters.
-// Counters start at zero and the last workgroup of a tile resets its counter,
-// so every launch finds them at zero.  Launches that overlap in time on one
-// device (unordered streams) must not both split K: they would share these.
-__device__ __align__(256) float g_gemv_part[kGemvPartFloats];
-__device__ __align__(256) uint32_t g_gemv_cnt[kGemvCounters];
-
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -221,11 +212,11 @@ struct Unit {
 
 // scale * sum over unit u of code * x, added to acc[t] for each of the MT
 // tokens (token t's activations start xs 32-bit words after token 0's; MT > 1
-// only with fp16 activations).  keep is all ones, or zero for a slot past
-// the wave's last unit (its sum is dropped bit-wise, so even an infinite or
-// NaN sum adds nothing).
+// only with fp16 activations).  keep is false for a slot past the wave's last
+// unit: the sums are then left as they were (a select, so a re-read unit
+// with an infinite or NaN scale changes nothing).
 template <int FMT, int XDT, int MT>
-__device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, size_t xs, int u, uint32_t keep,
+__device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, size_t xs, int u, bool keep,
                                          float (&acc)[MT]) {
     constexpr int E = unit_elems(FMT);
     float dot[MT];
@@ -255,31 +246,15 @@ __device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, siz
     if constexpr (fp32_scale(FMT)) d = __uint_as_float(b.s);
     else d = (float)__builtin_bit_cast(_Float16, uint16_t(b.s));
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = __builtin_fmaf(d, __uint_as_float(__float_as_uint(dot[t]) & keep), acc[t]);
+    for (int t = 0; t < MT; ++t) {
+        const float f = __builtin_fmaf(d, dot[t], acc[t]);
+        acc[t] = keep ? f : acc[t];
+    }
 }
 
 // Largest batch of units one wave loads before computing them (register
 // budget: the codes of a batch stay live).
 constexpr int unroll_cap(int fmt) { return fmt == kQ4_0 ? LQ_GEMV_UNR_Q4 : (fmt == kI8B64 ? LQ_GEMV_UNR_I8 : LQ_GEMV_UNR_Q8); }
-
-// sum_{j < S} p[j * pitch] in slice order, loads issued eight at a time so
-// their latencies overlap.
-__device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S) {
-    float t = 0.0f;
-    int j = 0;
-    for (; j < S; j += 8) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float* q = p + size_t(min(j + k, S - 1)) * pitch;
-            v[k] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (j + k < S) t += v[k];
-    }
-    return t;
-}
 
 // W waves per workgroup split a tile's K slice W ways (4, or 16 for
 // launches whose matrices would otherwise split K across 4+ workgroups: the
@@ -362,7 +337,7 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < UNR; ++k)
-            unit_fma<FMT, XDT, MT>(b[k], x, xs, min(u + k, ub - 1), u + k < ub ? ~0u : 0u, acc);
+            unit_fma<FMT, XDT, MT>(b[k], x, xs, min(u + k, ub - 1), u + k < ub, acc);
     }
 
 #pragma unroll
@@ -385,33 +360,22 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
         }
         return;
     }
-    // Split K: publish this slice, then the last arrival sums all slices.
+    // Split K: publish this slice, then the last arrival sums all slices in
+    // slice order (lq_splitk.h).  Slice j of token t sits at rows
+    // (j * MT + t) * pitch.
     const size_t pitch = size_t(D.tiles) * kTileRows;
-    // The partials and the counters are only touched by device-scope atomic
-    // accesses: loads and stores that go past the per-XCD L2 caches to the
-    // coherent memory side, and a read-modify-write that is atomic device
-    // wide.  So no fence is needed; on this chip an agent-scope fence writes
-    // back and invalidates a whole L2, which made split launches several
-    // times slower than the weight stream itself.  The store of the partials
-    // must have completed (s_waitcnt 0) before the counter moves, and the
-    // loads of the last arrival are issued only after its increment returned.
-    // Slice j of token t sits at rows (j * MT + t) * pitch.
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-        __hip_atomic_store(&D.part[(size_t(slice) * MT + t) * pitch + row], v[t], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    uint32_t prev = 0;
-    if (r == 0)
-        prev = __hip_atomic_fetch_add(&D.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != uint32_t(S - 1)) return;
+    for (int t = 0; t < MT; ++t) splitk_put(&D.part[(size_t(slice) * MT + t) * pitch + row], v[t]);
+    splitk_publish();
+    uint32_t last = 0;
+    if (r == 0) last = splitk_arrive(&D.cnt[tile], a.tag, S) ? 1u : 0u;
+    last = __builtin_amdgcn_readfirstlane(last);
+    if (!last) return;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const float y = sum_slices(D.part + size_t(t) * pitch + row, MT * pitch, S);
         if (r < nr) D.y[size_t(t) * N + row] = y;
     }
-    if (r == 0) __hip_atomic_store(&D.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // 16 weights (one code part) times 16 activations held in VGPRs: the sub-tile
@@ -639,32 +603,7 @@ hipError_t launch_sub_tokens(int xdt, int mt, const GemvArgs& a, hipStream_t str
     return launch_sub_unr<FMT, kF16, CAP, MT>(unr, a, stream);
 }
 
-std::mutex g_scratch_mu;
-float* g_part_addr[64] = {nullptr};
-uint32_t* g_cnt_addr[64] = {nullptr};
-
 }  // namespace
-
-hipError_t gemv_scratch(float** part, uint32_t** cnt) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lk(g_scratch_mu);
-    if (!g_part_addr[dev]) {
-        void* p = nullptr;
-        void* c = nullptr;
-        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_gemv_part));
-        if (e != hipSuccess) return e;
-        e = hipGetSymbolAddress(&c, HIP_SYMBOL(g_gemv_cnt));
-        if (e != hipSuccess) return e;
-        g_part_addr[dev] = static_cast<float*>(p);
-        g_cnt_addr[dev] = static_cast<uint32_t*>(c);
-    }
-    *part = g_part_addr[dev];
-    *cnt = g_cnt_addr[dev];
-    return hipSuccess;
-}
 
 hipError_t launch_gemv_sub(int fmt, int xdt, int mt, const GemvArgs& a, hipStream_t stream) {
     if (mt < 1 || mt > gemv_max_tokens(fmt) || (mt > 1 && xdt != kF16)) return hipErrorInvalidValue;

@@ -68,10 +68,14 @@ constexpr int kGemvThreads = 256;   // 4 waves: one tile, K split four ways
 #ifndef LQ_GEMV_WIDE_FROM
 #define LQ_GEMV_WIDE_FROM 4
 #endif
-// Split-K scratch held by the library on every device (static device arrays):
-// partial sums of the K slices of a tile, and one arrival counter per tile.
+// Split-K workspace of the GEMV calls (the caller's memory, lq_gemv_workspace_bytes):
+// one 64-bit arrival counter per tile of the split matrices, then the
+// partial sums of their K slices.  A launch splits K only if both fit.
+constexpr int64_t kGemvCounters = int64_t(1) << 16;     // 512 KiB
 constexpr int64_t kGemvPartFloats = int64_t(1) << 20;   // 4 MiB
-constexpr int64_t kGemvCounters = int64_t(1) << 16;
+constexpr size_t kGemvWorkspaceBytes = size_t(kGemvCounters) * 8 + size_t(kGemvPartFloats) * 4;
+// Most K slices of one tile (the arrival count is a 16-bit field).
+constexpr int64_t kMaxSlices = 4096;
 // Workgroups a launch aims for per CU before it splits K across workgroups,
 // and the fewest units a wave keeps when K is split.
 #ifndef LQ_GEMV_WGS_PER_CU
@@ -113,7 +117,7 @@ inline int gemv_min_units(int fmt) {
     return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kI8B64 ? LQ_GEMV_MIN_UNITS_I8 : LQ_GEMV_MIN_UNITS_Q8);
 }
 // The same for the multi-token GEMV, whose split K also moves M tokens of
-// partial sums per row through the scratch area.
+// partial sums per row through the workspace.
 inline int multi_min_units(int fmt) { return fmt == kI8B64 ? 2 : 8; }
 
 struct GemvDesc {
@@ -122,7 +126,7 @@ struct GemvDesc {
     const void* x;          // activations (fp32 or fp16): MT rows of K values
     float* y;               // MT rows of N outputs
     float* part;            // split-K partials: S slices x MT tokens x tiles * 64 floats (S > 1 only)
-    uint32_t* cnt;          // one arrival counter per tile (S > 1 only)
+    uint64_t* cnt;          // one arrival counter per tile (S > 1 only)
     int32_t N;              // rows
     int32_t nu;             // units per row (K / unit_elems)
     int32_t tiles;          // ceil(N / 64)
@@ -133,9 +137,14 @@ struct GemvDesc {
 
 struct GemvArgs {
     GemvDesc d[kMaxBatch];
+    uint64_t tag;           // this launch's split-K tag (splitk_arrive)
     int32_t count;
     int32_t total_wgs;
 };
+
+// A split-K tag for a new launch: nonzero, 48 bits, never repeated in the
+// process (a captured graph replays the tag it was captured with).
+uint64_t next_splitk_tag();
 
 // Most tokens one GEMV launch takes (MT > 1 only with fp16 activations).
 // Every weight is decoded once for all tokens, and each token adds one fp16
@@ -150,8 +159,6 @@ hipError_t launch_gemv(int fmt, int xdt, int waves, int mt, const GemvArgs& args
 // (args.total_wgs counts those workgroups, d[i].wg0 the first of matrix i,
 // d[i].S must be 1).
 hipError_t launch_gemv_sub(int fmt, int xdt, int mt, const GemvArgs& args, hipStream_t stream);
-// Device addresses of this device's split-K scratch (looked up once per device).
-hipError_t gemv_scratch(float** part, uint32_t** cnt);
 
 // ------------------------------------------------- multi-token GEMV ----
 constexpr int kMultiMaxTokens = 16;   // tokens of one MFMA fragment
@@ -178,7 +185,7 @@ struct MultiDesc {
     const _Float16* x;      // M x K activations, row-major
     float* y;               // M x N outputs, row-major
     float* part;            // split-K partials: S slices x M tokens x tiles * 64 floats (S > 1 only)
-    uint32_t* cnt;          // one arrival counter per tile (S > 1 only)
+    uint64_t* cnt;          // one arrival counter per tile (S > 1 only)
     int32_t N;              // rows (and the row pitch of y)
     int32_t K;              // reduction length (and the row pitch of x)
     int32_t nu;             // units per row
@@ -191,6 +198,7 @@ struct MultiDesc {
 
 struct MultiArgs {
     MultiDesc d[kMaxBatch];
+    uint64_t tag;           // this launch's split-K tag (splitk_arrive)
     int32_t count;
     int32_t total_wgs;
 };

@@ -17,7 +17,7 @@
 //     one of the fp16-tile GEMM.
 //   * A workgroup of 4 waves takes one 64-row tile and splits its units four
 //     ways (and K across workgroups when the matrix has few tiles), like the
-//     single-token GEMV, with the same split-K scratch.
+//     single-token GEMV, with the same split-K workspace hand-off.
 //   * Lane (r, g) (r = lane % 16, g = lane / 16) loads tile row 4r + g of a
 //     unit with one 16-byte load: the wave's load is the unit's contiguous
 //     1 KB run.  Four cross-row swaps (v_permlane32_swap, v_permlane16_swap)
@@ -34,6 +34,7 @@
 //     transposed as double dwords), so its activations are one 16-byte
 //     load.
 #include "lq_frag.h"
+#include "lq_splitk.h"
 
 namespace lq {
 namespace {
@@ -169,29 +170,13 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
     }
 }
 
-// sum_{j < S} p[j * pitch] in slice order (eight loads in flight).
-__device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S) {
-    float t = 0.0f;
-    for (int j = 0; j < S; j += 8) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            v[k] = __hip_atomic_load(p + size_t(min(j + k, S - 1)) * pitch, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (j + k < S) t += v[k];
-    }
-    return t;
-}
-
 // UNR: units whose loads one wave issues before computing them.
 template <int FMT, int UNR>
 __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArgs a) {
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
     __shared__ float red[4][16][64];
-    __shared__ uint32_t arrival;
+    __shared__ uint32_t last;
 
     // Matrix of this workgroup: the last descriptor whose first workgroup is
     // not after ours (uniform, scalar compares).
@@ -264,22 +249,19 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
         return;
     }
     // Split K: publish this slice, then the last workgroup to arrive adds the
-    // slices in slice order.  Partials and counter are accessed only with
-    // device-scope atomics (see the single-token GEMV for why no fence).
+    // slices in slice order (lq_splitk.h).
     const size_t pitch = size_t(D.tiles) * kTileRows;   // floats per token of one slice
     const size_t spitch = pitch * size_t(M);             // floats per slice
     if (token < M) {
         float* pp = D.part + size_t(slice) * spitch + size_t(token) * pitch + row0;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            __hip_atomic_store(pp + m, v[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int m = 0; m < 4; ++m) splitk_put(pp + m, v[m]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    splitk_publish();
     __syncthreads();
-    if (threadIdx.x == 0)
-        arrival = __hip_atomic_fetch_add(&D.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) last = splitk_arrive(&D.cnt[tile], a.tag, S) ? 1u : 0u;
     __syncthreads();
-    if (arrival != uint32_t(S - 1)) return;
+    if (!last) return;
     if (token < M) {
         const float* pp = D.part + size_t(token) * pitch + row0;
         float* yp = D.y + size_t(token) * size_t(N) + row0;
@@ -289,7 +271,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
             if (4 * r + m < nr) yp[m] = t;
         }
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&D.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

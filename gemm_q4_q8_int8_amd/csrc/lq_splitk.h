@@ -1,0 +1,73 @@
+// Device side of the GEMV split-K hand-off (single- and multi-token GEMV):
+// the workgroups of one 64-row tile each sum a K slice, publish it to the
+// caller's workspace, and the last one to arrive adds the slices in slice
+// order.  Not installed.
+//
+// Memory ordering on gfx950.  Partial sums are written with relaxed
+// agent-scope atomic stores and read with relaxed agent-scope atomic loads:
+// both bypass the per-XCD L2 (which is not coherent between XCDs) and are
+// performed at the device's coherence point.  A wave's vector memory counter
+// only drops once such a store is acknowledged there, so a wave that waits
+// for it (s_waitcnt 0) before its arrival RMW has made its partials visible
+// device-wide before the counter moves; the last arrival issues its loads
+// only after its RMW has returned.  Agent-scope release / acquire fences
+// would give the same order by writing back and invalidating a whole L2 per
+// workgroup, which made split launches several times slower.
+#pragma once
+
+#include "lq_internal.h"
+
+namespace lq {
+
+// Arrival of one K slice at its tile's counter; true for the last of S.  A
+// counter word is (tag << 16) | arrivals.  Every launch has a tag of its own
+// (next_splitk_tag), so a word holding anything else (zero, another launch's
+// count, bytes an unrelated call left in the workspace) counts as no
+// arrival yet: the workspace needs no clearing.  The last arrival clears
+// the word, so a captured graph, which replays one tag, finds it clear on
+// every replay.  The loop ends: a compare-and-swap fails only when another
+// arrival of the tile moved the word, at most S - 1 times.
+__device__ __forceinline__ bool splitk_arrive(uint64_t* cnt, uint64_t tag, int S) {
+    const uint64_t base = tag << 16;
+    uint64_t cur = 0;   // the usual state of a word before its first arrival
+    uint64_t next = base + 1;
+    while (!__hip_atomic_compare_exchange_strong(cnt, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+        next = ((cur & ~uint64_t(0xFFFF)) == base) ? cur + 1 : base + 1;
+    const bool last = (next & 0xFFFF) == uint64_t(S);
+    if (last) __hip_atomic_store(cnt, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return last;
+}
+
+// Store of one partial sum (see the ordering note above).
+__device__ __forceinline__ void splitk_put(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's partial-sum stores are performed device-wide; the
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void splitk_publish() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// sum_{j < S} p[j * pitch] in slice order, loads issued eight at a time so
+// their latencies overlap.
+__device__ __forceinline__ float sum_slices(const float* p, size_t pitch, int S) {
+    float t = 0.0f;
+    for (int j = 0; j < S; j += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float* q = p + size_t(min(j + k, S - 1)) * pitch;
+            v[k] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (j + k < S) t += v[k];
+    }
+    return t;
+}
+
+}  // namespace lq

@@ -55,12 +55,19 @@
  * Conventions for every call.
  *   - Pointers named W, x, X, y, Y, out, dst, src, codes, scales, ws are
  *     DEVICE pointers (memory the caller allocated on the current HIP device);
- *     `descs` of lq_gemv_batch is a HOST pointer.  The caller owns every
- *     buffer; the library keeps no pointer after a call returns and allocates
- *     no device memory.  It holds one static scratch area per device (4 MiB
- *     of partial sums and 256 KiB of counters, part of the loaded code
- *     object) that lq_gemv / lq_gemv_batch / lq_gemv_multi use when they
- *     split K across workgroups.
+ *     `descs` of the batch calls is a HOST pointer.  The caller owns every
+ *     buffer and the library borrows them for the call, as the "oxinfer"
+ *     page's loader borrows quantized weights in place ("Pre-quantized
+ *     checkpoints": QBuf, no copy); it keeps no pointer after a call returns
+ *     and allocates no device memory.
+ *   - Workspaces.  Calls that may split K across workgroups take an optional
+ *     `ws` / `ws_bytes`: the GEMV calls (lq_gemv_workspace_bytes() bytes,
+ *     any contents: no clearing needed, every call leaves it reusable; without
+ *     one a GEMV keeps each tile's K inside one workgroup, which is correct
+ *     but slower for matrices of few rows) and the GEMM calls
+ *     (lq_gemm_workspace_bytes()).  Calls that run at the same time on
+ *     different streams need workspaces of their own; calls on one stream may
+ *     share one.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *     Calls only enqueue work (no implicit synchronisation); results are
  *     ready when the stream reaches that point.
@@ -75,11 +82,11 @@
  *     before any HIP call, so a rejected call touches no device state.  On a
  *     failure lq_last_error() returns a message for the calling thread.
  *     Nothing aborts, prints or throws across the ABI.
- *   - Thread safety: calls may come from several host threads; calls that
- *     write the same buffers must be ordered by the caller.  GEMV calls on
- *     one device share that device's split-K scratch: GEMV work enqueued on
- *     different streams must not run at the same time (order the streams
- *     with events); GEMV calls on one stream are always safe.
+ *   - Thread safety: the library holds no state besides a per-device record
+ *     of compute-unit counts and a counter of launch tags, both guarded, so
+ *     calls may come from several host threads on several streams.  Calls
+ *     that write the same buffers (outputs, workspaces) must be ordered by
+ *     the caller.
  */
 #ifndef LQ_H
 #define LQ_H
@@ -91,7 +98,7 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 6
+#define LQ_ABI_VERSION 7
 
 typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2, LQ_I8B32 = 3 } lq_fmt;
 /* Activation and source dtypes.  LQ_BF16 is accepted only as the source of
@@ -149,16 +156,23 @@ lq_status lq_repack_gguf(int32_t fmt, const void* src, void* dst,
 lq_status lq_pack_planes(int32_t fmt, const void* codes, const void* scales,
                          void* dst, int64_t N, int64_t K, void* stream);
 
-/* Unpacked weights: out[n*K + k] = RN_fp32(w[n,k]).  Exact for Q4_0 and Q8_0
- * (the product of a small integer and an fp16 scale fits fp32); one IEEE
- * rounding of c * s for LQ_I8B64 and LQ_I8B32.  out: N*K fp32, 16-byte
- * aligned. */
+/* Unpacked weights: out[n*K + k] = RN_fp32(w[n,k]), the value each block
+ * defines ("lean" page, model table: GGUF Q4_0 / Q8_0 blocks; "oxinfer" page,
+ * "How it works", quant.rs: 32 weights per scale, two nibbles per byte with
+ * an f16 scale; "wgpu-llm" page, "INT8 mode": int8 with block size 64).
+ * Exact for Q4_0 and Q8_0 (the product of a small integer and an fp16 scale
+ * fits fp32); one IEEE rounding of c * s for LQ_I8B64 and LQ_I8B32.  out:
+ * N*K fp32, 16-byte aligned. */
 lq_status lq_dequant_f32(int32_t fmt, const void* W, float* out,
                          int64_t N, int64_t K, void* stream);
 
 /* Unpacked weights rounded once to fp16 (bit patterns): out[n*K + k] =
- * RN_fp16(w[n,k]), round to nearest even, subnormals kept, overflow to inf.
- * This is the tile contract of lq_gemm.  out: N*K uint16, 16-byte aligned. */
+ * RN_fp16(w[n,k]), rounded from the exact value, round to nearest even,
+ * subnormals kept, overflow to inf.  This is the weight tile the prefill GEMM
+ * multiplies for LQ_Q4_0 / LQ_Q8_0 (the "oxinfer" page's GPU GEMMs dequantize
+ * each weight tile on chip before the dense product: "Platforms and
+ * accelerators"; here in fp16 for the matrix cores).  out: N*K uint16,
+ * 16-byte aligned. */
 lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out,
                          int64_t N, int64_t K, void* stream);
 
@@ -180,11 +194,24 @@ lq_status lq_dequant_f16(int32_t fmt, const void* W, uint16_t* out,
 lq_status lq_quantize(int32_t fmt, const void* src, int32_t sdt, void* W,
                       int64_t N, int64_t K, void* stream);
 
+/* Bytes of a GEMV split-K workspace (the same for every shape): 64-bit
+ * arrival counters and fp32 partial sums.  Any contents are valid input; a
+ * call leaves it reusable by the next call on the same stream. */
+size_t lq_gemv_workspace_bytes(void);
+
 /* Decode GEMV: y[n] = sum_k w[n,k] * x[k] for n < N, accumulated in fp32 with
- * the weights decoded exactly.  W: packed N x K; x: K values of dtype xdt;
- * y: N fp32.  Accuracy: |y - y_exact| <= 1e-4 * sum_k |w x| + 1e-6 per row. */
+ * the weights decoded exactly.  Decode streams every dense weight once per
+ * token and is bound by memory bandwidth ("oxinfer" page, "Performance"); its
+ * kernels take the quantized blocks directly ("How it works", quant.rs).
+ * W: packed N x K; x: K values of dtype xdt; y: N fp32.  ws / ws_bytes: a
+ * GEMV workspace (above) or NULL / 0.  Accuracy: |y - y_exact| <= 1e-4 *
+ * sum_k |w x| + 1e-6 per row.  A NaN scale makes the rows it enters NaN; an
+ * infinite scale makes them non-finite (see the readings in the design
+ * notes: the scale multiplies each block's exact sum, so where the per-weight
+ * expansion gives NaN the result may be +-inf). */
 lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt,
-                  float* y, int64_t N, int64_t K, void* stream);
+                  float* y, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* One independent GEMV for lq_gemv_batch (fields as in lq_gemv). */
 typedef struct lq_gemv_desc {
@@ -198,10 +225,15 @@ typedef struct lq_gemv_desc {
 } lq_gemv_desc;
 
 /* Grouped launch of `count` independent GEMVs (for example every projection of
- * a decoder layer), so that small matrices share launches.  descs: HOST array
- * of `count` descriptors (count >= 1), read during the call only.  Every
+ * a decoder layer), so that small matrices share launches: a decode step
+ * issues many small parallel regions whose dispatch cost matters ("oxinfer"
+ * page, "How it works", pool.rs).  descs: HOST array of `count` descriptors
+ * (count >= 1), read during the call only; descriptors of one format and
+ * activation dtype run in one kernel launch (up to 16 per launch).  ws /
+ * ws_bytes as in lq_gemv (one workspace serves the whole call).  Every
  * descriptor is validated before anything is enqueued. */
-lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
+lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Multi-token GEMV, the decode step of a few tokens at once (verification of
  * drafted tokens: "oxinfer" page, "Speculative decoding", and the multi-token
@@ -214,10 +246,11 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* stream);
  * for more tokens on the matrix cores.  W: packed N x K; X: M x K fp16
  * row-major (xdt must be LQ_F16, else LQ_ERR_UNSUPPORTED); Y: M x N fp32
  * row-major.  1 <= M <= 16, else LQ_ERR_SHAPE.  Accuracy as lq_gemv, per
- * output: |Y - Y_exact| <= 1e-4 * sum_k |w x| + 1e-6.  Shares the GEMV
- * split-K scratch (see thread safety above). */
+ * output: |Y - Y_exact| <= 1e-4 * sum_k |w x| + 1e-6.  ws / ws_bytes: a GEMV
+ * workspace or NULL / 0, as in lq_gemv. */
 lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt,
-                        float* Y, int64_t M, int64_t N, int64_t K, void* stream);
+                        float* Y, int64_t M, int64_t N, int64_t K, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* One independent multi-token GEMV for lq_gemv_multi_batch (fields as in
  * lq_gemv_multi; M may differ between descriptors). */
@@ -238,10 +271,16 @@ typedef struct lq_gemv_multi_desc {
  * (count >= 1), read during the call only; all are validated before anything
  * is enqueued.  Descriptors of one format run in one kernel launch (up to 16
  * per launch), except that each M run on the lq_gemv kernel (see
- * lq_gemv_multi) takes a launch of its own. */
-lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* stream);
+ * lq_gemv_multi) takes a launch of its own.  ws / ws_bytes as in lq_gemv. */
+lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* ws,
+                              size_t ws_bytes, void* stream);
 
-/* Workspace bytes lq_gemm needs for these arguments (0 means none). */
+/* Workspace bytes lq_gemm needs for these arguments (0 means none): the fp32
+ * partial products of K slices when the GEMM splits K across workgroups.
+ * Like every buffer it is the caller's memory, borrowed for the call (the
+ * "oxinfer" page's host owns GPU memory and the module only borrows it:
+ * "Browser (WebGPU)", gpu_upload / gpu_matmul; "Pre-quantized checkpoints",
+ * QBuf). */
 size_t lq_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 
 /* Prefill GEMM ("oxinfer" page, "Performance": prefill is compute bound;
@@ -284,11 +323,13 @@ lq_status lq_gemm_batch(int32_t fmt, const void* X, int32_t xdt, int64_t M, int6
                         const lq_gemm_desc* descs, int32_t count,
                         void* ws, size_t ws_bytes, void* stream);
 
-/* Route by token count, after the "oxinfer" page's rule that GPU matmul
- * kernels take only prompt-sized work ("Platforms and accelerators": t >= 16
- * tokens): M == 1 runs lq_gemv on X (fp32 or fp16); 2 <= M <= 16 with fp16 X
- * runs lq_gemv_multi; everything else runs lq_gemm.  Arguments as in
- * lq_gemm. */
+/* Route by token count, after the "oxinfer" page's rule that the dense-tile
+ * GPU matmul takes only prompt-sized work ("Platforms and accelerators": t >=
+ * 16 tokens): M == 1 runs lq_gemv on X (fp32 or fp16); 2 <= M <= 16 with fp16
+ * X runs lq_gemv_multi (its matrix-core fragment holds 16 tokens, and it is
+ * faster than the tile GEMM there); everything else runs lq_gemm.  Arguments
+ * as in lq_gemm; the GEMV paths use ws as their workspace when ws_bytes >=
+ * lq_gemv_workspace_bytes(), else none. */
 lq_status lq_matmul(int32_t fmt, const void* W, const void* X, int32_t xdt,
                     float* Y, int64_t M, int64_t N, int64_t K,
                     void* ws, size_t ws_bytes, void* stream);

@@ -58,10 +58,24 @@ def check_guard(buf, n):
     assert np.all(tail == SENTINEL), "write past the end of the output buffer"
 
 
-def gemv(fmt: str, Wd, x: np.ndarray, N, K):
+_WS = {}
+
+
+def gemv_ws(key=0):
+    """A GEMV split-K workspace (lq_gemv_workspace_bytes() bytes), one per key
+    and device, filled with garbage once: the library needs no clearing."""
+    dev = torch.cuda.current_device()
+    if (dev, key) not in _WS:
+        _WS[(dev, key)] = torch.full((lq.lq_gemv_workspace_bytes(),), 0xA5, dtype=torch.uint8, device="cuda")
+    return _WS[(dev, key)]
+
+
+def gemv(fmt: str, Wd, x: np.ndarray, N, K, ws=True):
+    """y = W x through lq_gemv; ws=True passes the shared workspace (K may be
+    split across workgroups), ws=None runs without one."""
     xd = to_device(x)
     y = guarded(N)
-    lq.lq_gemv(FMT[fmt], Wd, xd, y, N, K)
+    lq.lq_gemv(FMT[fmt], Wd, xd, y, N, K, ws=gemv_ws() if ws is True else ws)
     torch.cuda.synchronize()
     check_guard(y, N)
     return y[:N].cpu().numpy()
@@ -85,10 +99,10 @@ def ratio(y, yref, S, rel, abs_):
     return float(np.max(np.abs(y - yref) / (rel * S + abs_))) if y.size else 0.0
 
 
-def gemv_multi(fmt: str, Wd, X: np.ndarray, M, N, K):
+def gemv_multi(fmt: str, Wd, X: np.ndarray, M, N, K, ws=True):
     Xd = to_device(X)
     Y = guarded(M * N)
-    lq.lq_gemv_multi(FMT[fmt], Wd, Xd, Y, M, N, K)
+    lq.lq_gemv_multi(FMT[fmt], Wd, Xd, Y, M, N, K, ws=gemv_ws() if ws is True else ws)
     torch.cuda.synchronize()
     check_guard(Y, M * N)
     return Y[:M * N].cpu().numpy().reshape(M, N)

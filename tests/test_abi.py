@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 6
+    assert lq.lq_abi_version() == 7
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -70,26 +70,34 @@ A16 = 0x100000     # a 16-byte aligned address that is never dereferenced: every
 
 def test_rejections_before_any_hip_call(L):
     g = L
-    assert g.lq_gemv(9, A16, A16, 0, A16, 4, 32, None) == FMT
-    assert g.lq_gemv(0, A16, A16, 0, A16, 0, 32, None) == SHAPE
-    assert g.lq_gemv(0, A16, A16, 0, A16, -3, 32, None) == SHAPE
-    assert g.lq_gemv(0, A16, A16, 0, A16, 4, 48, None) == SHAPE
-    assert g.lq_gemv(2, A16, A16, 0, A16, 4, 96, None) == SHAPE       # int8 block 64
-    assert g.lq_gemv(0, A16, A16, 0, A16, 4, 2**25 + 32, None) == SHAPE   # K above 2^25
-    assert g.lq_gemv(0, A16, A16, 0, A16, 2 ** 31, 32, None) == SHAPE
-    assert g.lq_gemv(0, None, A16, 0, A16, 4, 32, None) == ARG
-    assert g.lq_gemv(0, A16 + 8, A16, 0, A16, 4, 32, None) == ALIGN
-    assert g.lq_gemv(0, A16, A16 + 4, 0, A16, 4, 32, None) == ALIGN
-    assert g.lq_gemv(0, A16, A16, 0, A16 + 2, 4, 32, None) == ALIGN
-    assert g.lq_gemv(0, A16, A16, 5, A16, 4, 32, None) == DTYPE
+    assert g.lq_gemv(9, A16, A16, 0, A16, 4, 32, None, 0, None) == FMT
+    assert g.lq_gemv(0, A16, A16, 0, A16, 0, 32, None, 0, None) == SHAPE
+    assert g.lq_gemv(0, A16, A16, 0, A16, -3, 32, None, 0, None) == SHAPE
+    assert g.lq_gemv(0, A16, A16, 0, A16, 4, 48, None, 0, None) == SHAPE
+    assert g.lq_gemv(2, A16, A16, 0, A16, 4, 96, None, 0, None) == SHAPE       # int8 block 64
+    assert g.lq_gemv(0, A16, A16, 0, A16, 4, 2**25 + 32, None, 0, None) == SHAPE   # K above 2^25
+    assert g.lq_gemv(0, A16, A16, 0, A16, 2 ** 31, 32, None, 0, None) == SHAPE
+    assert g.lq_gemv(0, None, A16, 0, A16, 4, 32, None, 0, None) == ARG
+    assert g.lq_gemv(0, A16 + 8, A16, 0, A16, 4, 32, None, 0, None) == ALIGN
+    assert g.lq_gemv(0, A16, A16 + 4, 0, A16, 4, 32, None, 0, None) == ALIGN
+    assert g.lq_gemv(0, A16, A16, 0, A16 + 2, 4, 32, None, 0, None) == ALIGN
+    assert g.lq_gemv(0, A16, A16, 5, A16, 4, 32, None, 0, None) == DTYPE
     assert "dtype" in lq.lq_last_error()
     # batch: count and per-descriptor validation
     d = (lq.lq_gemv_desc * 2)()
     d[0] = lq.lq_gemv_desc(0, 0, A16, A16, A16, 4, 32)
     d[1] = lq.lq_gemv_desc(0, 0, A16, A16, A16, 4, 40)
-    assert g.lq_gemv_batch(d, 0, None) == ARG
-    assert g.lq_gemv_batch(None, 1, None) == ARG
-    assert g.lq_gemv_batch(d, 2, None) == SHAPE
+    assert g.lq_gemv_batch(d, 0, None, 0, None) == ARG
+    assert g.lq_gemv_batch(None, 1, None, 0, None) == ARG
+    assert g.lq_gemv_batch(d, 2, None, 0, None) == SHAPE
+    # GEMV workspace: optional, but when given at least lq_gemv_workspace_bytes(), 16-byte aligned
+    wsb = lq.lq_gemv_workspace_bytes()
+    assert wsb == (1 << 16) * 8 + (1 << 20) * 4
+    d[1] = lq.lq_gemv_desc(0, 0, A16, A16, A16, 4, 64)
+    assert g.lq_gemv_batch(d, 2, A16, wsb - 1, None) == WS
+    assert g.lq_gemv_batch(d, 2, A16 + 8, wsb, None) == ALIGN
+    assert g.lq_gemv(0, A16, A16, 0, A16, 4, 32, A16, 64, None) == WS
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 4, 64, 32, A16, 16, None) == WS
     # gemm
     assert g.lq_gemm(0, A16, A16, 0, A16, 16, 32, 32, None, 0, None) == UNSUP     # fp32 X
     assert g.lq_gemm(2, A16, A16, 1, A16, 16, 32, 32, None, 0, None) == SHAPE     # int8 block 64
@@ -114,24 +122,24 @@ def test_rejections_before_any_hip_call(L):
     gd[1] = lq.lq_gemm_desc(A16, None, 64)
     assert g.lq_gemm_batch(0, A16, 1, 16, 64, gd, 2, None, 0, None) == ARG
     # multi-token GEMV: fp16 activations, 1 <= M <= 16
-    assert g.lq_gemv_multi(0, A16, A16, 0, A16, 4, 64, 32, None) == UNSUP
-    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 0, 64, 32, None) == SHAPE
-    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 17, 64, 32, None) == SHAPE
-    assert g.lq_gemv_multi(2, A16, A16, 1, A16, 4, 64, 32, None) == SHAPE   # int8 block 64
-    assert g.lq_gemv_multi(9, A16, A16, 1, A16, 4, 64, 32, None) == FMT
-    assert g.lq_gemv_multi(0, A16, A16 + 8, 1, A16, 4, 64, 32, None) == ALIGN
-    assert g.lq_gemv_multi(0, A16, A16, 1, A16 + 1, 4, 64, 32, None) == ALIGN
-    assert g.lq_gemv_multi(0, A16, None, 1, A16, 4, 64, 32, None) == ARG
-    assert g.lq_gemv_multi(0, A16, A16, 3, A16, 4, 64, 32, None) == DTYPE
+    assert g.lq_gemv_multi(0, A16, A16, 0, A16, 4, 64, 32, None, 0, None) == UNSUP
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 0, 64, 32, None, 0, None) == SHAPE
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16, 17, 64, 32, None, 0, None) == SHAPE
+    assert g.lq_gemv_multi(2, A16, A16, 1, A16, 4, 64, 32, None, 0, None) == SHAPE   # int8 block 64
+    assert g.lq_gemv_multi(9, A16, A16, 1, A16, 4, 64, 32, None, 0, None) == FMT
+    assert g.lq_gemv_multi(0, A16, A16 + 8, 1, A16, 4, 64, 32, None, 0, None) == ALIGN
+    assert g.lq_gemv_multi(0, A16, A16, 1, A16 + 1, 4, 64, 32, None, 0, None) == ALIGN
+    assert g.lq_gemv_multi(0, A16, None, 1, A16, 4, 64, 32, None, 0, None) == ARG
+    assert g.lq_gemv_multi(0, A16, A16, 3, A16, 4, 64, 32, None, 0, None) == DTYPE
     assert g.lq_matmul(0, A16, A16, 1, A16, 4, 64, 48, None, 0, None) == SHAPE
     md = (lq.lq_gemv_multi_desc * 2)()
     md[0] = lq.lq_gemv_multi_desc(0, 1, A16, A16, A16, 4, 64, 32)
     md[1] = lq.lq_gemv_multi_desc(1, 1, A16, A16, A16, 17, 64, 32)
-    assert g.lq_gemv_multi_batch(md, 0, None) == ARG
-    assert g.lq_gemv_multi_batch(None, 1, None) == ARG
-    assert g.lq_gemv_multi_batch(md, 2, None) == SHAPE          # second descriptor: M = 17
+    assert g.lq_gemv_multi_batch(md, 0, None, 0, None) == ARG
+    assert g.lq_gemv_multi_batch(None, 1, None, 0, None) == ARG
+    assert g.lq_gemv_multi_batch(md, 2, None, 0, None) == SHAPE          # second descriptor: M = 17
     md[1] = lq.lq_gemv_multi_desc(1, 0, A16, A16, A16, 4, 64, 32)
-    assert g.lq_gemv_multi_batch(md, 2, None) == UNSUP          # fp32 activations
+    assert g.lq_gemv_multi_batch(md, 2, None, 0, None) == UNSUP          # fp32 activations
     assert "descriptor 1" in lq.lq_last_error()
     # load-time quantization
     assert g.lq_quantize(9, A16, 0, A16, 4, 64, None) == FMT
@@ -146,6 +154,19 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_pack_planes(2, A16, None, A16, 4, 64, None) == ARG
     assert g.lq_dequant_f32(0, A16, A16 + 4, 4, 64, None) == ALIGN
     assert g.lq_dequant_f16(1, A16, A16, 4, 33, None) == SHAPE
+
+
+def test_gemm_accepts_activations_above_4gib(L):
+    """X of M K 2 >= 2^32 bytes is a valid GEMM (byte offsets into X are
+    64-bit): on a machine without a GPU the call gets past every argument
+    check and fails only at the first HIP call."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would run (the GPU tests cover it)")
+    M, N, K = (1 << 20) + 37, 64, 2048
+    assert lq.lq_gemm_workspace_bytes(lq.LQ_Q4_0, M, N, K) == 0
+    assert L.lq_gemm(0, A16, A16, 1, A16, M, N, K, None, 0, None) == HIP
+    assert L.lq_gemm(0, A16, A16, 1, A16, 1 << 22, 64, 1 << 13, None, 0, None) == HIP   # 64 GiB of X
 
 
 def test_init_without_device_reports_hip_error(L):

@@ -89,7 +89,8 @@ def test_int8_decoder_layer_launches(oracle):
     for group in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"]):
         say("int8 layer launch", group)
         ys = {n: gu.guarded(mats[n].N) for n in group}
-        lq.lq_gemv_batch([(lq.LQ_I8B64, Wd[n], xd[mats[n].xkey], ys[n], mats[n].N, mats[n].K) for n in group])
+        lq.lq_gemv_batch([(lq.LQ_I8B64, Wd[n], xd[mats[n].xkey], ys[n], mats[n].N, mats[n].K) for n in group],
+                         ws=gu.gemv_ws())
         torch.cuda.synchronize()
         for n in group:
             m = mats[n]

@@ -171,7 +171,7 @@ def test_multi_batch_mixed(oracle):
         devs.append((Wd, Xd))
         descs.append((gu.FMT[fmt], Wd, Xd, Y, M, N, K))
         outs.append(Y)
-    lq.lq_gemv_multi_batch(descs)
+    lq.lq_gemv_multi_batch(descs, ws=gu.gemv_ws())
     torch.cuda.synchronize()
     for (fmt, M, N, K, w, s, X), Y, (Wd, Xd) in zip(cases, outs, devs):
         gu.check_guard(Y, M * N)
@@ -192,7 +192,7 @@ def test_matmul_routes_few_tokens_to_multi():
         X = lqgen.activations(13 + M, M * K, np.float16).reshape(M, K)
         Ym = gu.gemv_multi("q4_0", Wd, X, M, N, K)
         Y = gu.guarded(M * N)
-        lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(X), Y, M, N, K)
+        lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(X), Y, M, N, K, ws=gu.gemv_ws())
         torch.cuda.synchronize()
         gu.check_guard(Y, M * N)
         assert np.array_equal(Y[:M * N].cpu().numpy().reshape(M, N), Ym), M
@@ -212,7 +212,7 @@ def test_multi_graph_replays_match_eager(oracle):
 
     def run():
         for (fmt, M, N, K, _, _, _, Wd, Xd), Y in zip(data, outs):
-            lq.lq_gemv_multi(gu.FMT[fmt], Wd, Xd, Y, M, N, K)
+            lq.lq_gemv_multi(gu.FMT[fmt], Wd, Xd, Y, M, N, K, ws=gu.gemv_ws())
 
     run()
     torch.cuda.synchronize()
@@ -286,7 +286,7 @@ def _grouped_workload(oracle, wl, sample):
         descs.append((gu.FMT[m.fmt], Wd, Xd[m.xkey], Y, M, m.N, m.K))
         outs.append(Y)
     say("gemv_multi grouped workload", wl.name, M, len(mats))
-    lq.lq_gemv_multi_batch(descs)
+    lq.lq_gemv_multi_batch(descs, ws=gu.gemv_ws())
     torch.cuda.synchronize()
     for (m, w, s), Y in zip(mats, outs):
         gu.check_guard(Y, M * m.N)

@@ -188,7 +188,7 @@ def test_gemv_batch_mixed(oracle):
         y = gu.guarded(N)
         descs.append((gu.FMT[fmt], Wd, xd, y, N, K))
         outs.append(y)
-    lq.lq_gemv_batch(descs)
+    lq.lq_gemv_batch(descs, ws=gu.gemv_ws())
     torch.cuda.synchronize()
     for (fmt, N, K, w, s, x), y in zip(cases, outs):
         gu.check_guard(y, N)
@@ -220,8 +220,8 @@ def test_graph_replays_match_eager(oracle):
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
 
     def run():
-        lq.lq_gemv_batch([descs[0]])
-        lq.lq_gemv_batch(descs[1:])
+        lq.lq_gemv_batch([descs[0]], ws=gu.gemv_ws())
+        lq.lq_gemv_batch(descs[1:], ws=gu.gemv_ws())
         lq.lq_gemm(lq.LQ_Q4_0, Wg, Xg, Yg, M, Ng, Kg, ws=ws, ws_bytes=wsb)
 
     outs = [d[3] for d in descs] + [Yg]
@@ -310,10 +310,10 @@ def _run_workload_rows(oracle, wl, sample=None, batch=True):
         descs.append((gu.FMT[m.fmt], Wd, xd, y, m.N, m.K))
         outs.append(y)
     if batch:
-        lq.lq_gemv_batch(descs)
+        lq.lq_gemv_batch(descs, ws=gu.gemv_ws())
     else:
         for d in descs:
-            lq.lq_gemv(d[0], d[1], d[2], d[3], d[4], d[5])
+            lq.lq_gemv(d[0], d[1], d[2], d[3], d[4], d[5], ws=gu.gemv_ws())
     torch.cuda.synchronize()
     worst = 0.0
     for (m, w, s), y in zip(mats, outs):
@@ -346,15 +346,18 @@ def test_workload_q8_0_layer(oracle):
 
 @pytest.mark.slow
 def test_workload_q4_0_lm_head(oracle):
-    say("workload q4_0 LM head 151936x896 + FFN")
-    _run_workload_rows(oracle, lqgen.q4_0_lmhead_151936x896(), sample=8192, batch=False)
+    """Every one of the 151,936 LM-head rows (and both FFN matrices)."""
+    say("workload q4_0 LM head 151936x896 + FFN, every row")
+    _run_workload_rows(oracle, lqgen.q4_0_lmhead_151936x896(), batch=False)
 
 
 @pytest.mark.slow
 def test_workload_i8b64_layers(oracle):
+    """The first and last TinyLlama layers, every row, grouped as bench.py
+    groups the whole set."""
     for layer in (0, 21):
-        say("workload i8b64 TinyLlama layer", layer)
-        _run_workload_rows(oracle, lqgen.i8b64_tinyllama_layer(layer), sample=1024, batch=True)
+        say("workload i8b64 TinyLlama layer", layer, "every row")
+        _run_workload_rows(oracle, lqgen.i8b64_tinyllama_layer(layer), batch=True)
 
 
 # ---------------------------------------------------------------- GEMM ----
@@ -472,44 +475,59 @@ def test_matmul_routes_by_token_count():
     x = lqgen.activations(13, K, np.float16)
     y1 = gu.gemv("q4_0", Wd, x, N, K)
     Y = gu.guarded(N)
-    lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(x), Y, 1, N, K)
+    lq.lq_matmul(lq.LQ_Q4_0, Wd, to_device(x), Y, 1, N, K, ws=gu.gemv_ws())
     torch.cuda.synchronize()
     assert np.array_equal(Y[:N].cpu().numpy(), y1)
+
+
+def _prefill_ffn_all_outputs(oracle, fmt, fid, mats, X, M):
+    """gate and up through one lq_gemm_batch launch, down through lq_gemm
+    (K split across workgroups, workspace and ordered reduction), as bench.py
+    times them; every output against the oracle at the GEMM bar."""
+    byname = {name: (w, s, N, K) for name, w, s, N, K in mats}
+    Wd = {name: gu.upload(fmt, w, s, N, K) for name, (w, s, N, K) in byname.items()}
+    gate, up, down = byname["gate"], byname["up"], byname["down"]
+    Xd = to_device(X["in"])
+    Yg, Yu = gu.guarded(M * gate[2]), gu.guarded(M * up[2])
+    say("gemm workload", fmt, "gate+up (one launch)", M, gate[2], gate[3])
+    lq.lq_gemm_batch(fid, Xd, M, gate[3], [(Wd["gate"], Yg, gate[2]), (Wd["up"], Yu, up[2])])
+    say("gemm workload", fmt, "down", M, down[2], down[3])
+    wsb = lq.lq_gemm_workspace_bytes(fid, M, down[2], down[3])
+    assert wsb > 0, "down is meant to split K"
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    Yd = gu.guarded(M * down[2])
+    lq.lq_gemm(fid, Wd["down"], to_device(X["down"]), Yd, M, down[2], down[3], ws=ws)
+    torch.cuda.synchronize()
+    for name, Y, xk in (("gate", Yg, "in"), ("up", Yu, "in"), ("down", Yd, "down")):
+        w, s, N, K = byname[name]
+        gu.check_guard(Y, M * N)
+        Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X[xk], M, N, K)
+        r = gu.ratio(Y[:M * N].cpu().numpy().reshape(M, N), Yr, S, gu.GEMM_REL, gu.GEMM_ABS)
+        assert r <= 1.0, (fmt, name, r)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("fmt", ["q8_0", "i8b64", "i8b32"])
 def test_workload_int8_prefill(oracle, fmt):
-    """The prefill FFN shapes (2048 / 11008, M = 512) with int8 weights:
-    sampled outputs against the exact product at the GEMM bar."""
+    """The prefill FFN shapes (2048 / 11008, M = 512) with int8 weights,
+    every output against the exact product at the GEMM bar."""
     M = 512
-    for name, N, K in (("gate", 11008, 2048), ("down", 2048, 11008)):
-        say("gemm workload", fmt, name, M, N, K)
-        w, s = make(fmt, 4400 + N, N, K)
-        X = lqgen.activations(4500 + K, M * K, np.float16).reshape(M, K)
-        Wd = gu.upload(fmt, w, s, N, K)
-        Y = gu.gemm(Wd, X, M, N, K, fmt)
-        rng = np.random.default_rng(N + K)
-        ms = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 511], rng.integers(0, M, 25)]))
-        ns = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, N - 1], rng.integers(0, N, 120)]))
-        Yr, S = oracle.gemm(ORACLE_FMT[fmt], w, s, X, M, N, K, ms=ms, ns=ns)
-        r = gu.ratio(Y[np.ix_(ms, ns)], Yr, S, gu.GEMM_REL, gu.GEMM_ABS)
-        assert r <= 1.0, (fmt, name, r)
+    mats = []
+    for name, N, K in (("gate", 11008, 2048), ("up", 11008, 2048), ("down", 2048, 11008)):
+        w, s = make(fmt, 4400 + N + (1 if name == "up" else 0), N, K)
+        mats.append((name, w, s, N, K))
+    X = {"in": lqgen.activations(4500 + 2048, M * 2048, np.float16).reshape(M, 2048),
+         "down": lqgen.activations(4500 + 11008, M * 11008, np.float16).reshape(M, 11008)}
+    _prefill_ffn_all_outputs(oracle, fmt, gu.FMT[fmt], mats, X, M)
 
 
 @pytest.mark.slow
 def test_workload_q4_0_prefill_ffn(oracle):
+    """The Q4_0 prefill FFN (2048 / 11008, M = 512) in bench.py's launches,
+    every one of its 512 x (11008 + 11008 + 2048) outputs."""
     wl = lqgen.q4_0_prefill_ffn_2048x11008(512)
-    M = wl.M
-    for m in wl.mats:
-        say("gemm workload", m.name, M, m.N, m.K)
-        w, _ = m.generate()
-        X = wl.x(m.xkey)
-        Wd = gu.upload("q4_0", w, None, m.N, m.K)
-        Y = gu.gemm(Wd, X, M, m.N, m.K)
-        rng = np.random.default_rng(m.seed)
-        ms = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 511], rng.integers(0, M, 25)]))
-        ns = np.unique(np.concatenate([[0, 1, 127, 128, m.N - 1], rng.integers(0, m.N, 120)]))
-        Yr, S = oracle.gemm(0, w, None, X, M, m.N, m.K, ms=ms, ns=ns)
-        r = gu.ratio(Y[np.ix_(ms, ns)], Yr, S, gu.GEMM_REL, gu.GEMM_ABS)
-        assert r <= 1.0, (m.name, r)
+    mats = [(m.name, m.generate()[0], None, m.N, m.K) for m in wl.mats]
+    keys = {m.name: m.xkey for m in wl.mats}
+    X = {"in": wl.x(keys["gate"]), "down": wl.x(keys["down"])}
+    assert keys["gate"] == keys["up"]
+    _prefill_ffn_all_outputs(oracle, "q4_0", lq.LQ_Q4_0, mats, X, wl.M)
