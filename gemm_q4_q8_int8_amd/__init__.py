@@ -22,7 +22,8 @@ FORMATS = {"q4_0": LQ_Q4_0, "q8_0": LQ_Q8_0, "i8b64": LQ_I8B64, "i8b32": LQ_I8B3
 # Every symbol include/lq.h declares.
 EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq_scale_offset",
            "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_quantize", "lq_dequant_f32",
-           "lq_dequant_f16", "lq_gemv_workspace_bytes", "lq_gemv", "lq_gemv_batch", "lq_gemv_multi",
+           "lq_dequant_f16", "lq_gemv_workspace_bytes", "lq_gemv", "lq_gemv_batch",
+           "lq_gemv_batch_noalloc", "lq_gemv_multi",
            "lq_gemv_multi_batch", "lq_gemm_workspace_bytes",
            "lq_gemm", "lq_gemm_batch",
            "lq_matmul", "lq_status_str", "lq_last_error")
@@ -85,6 +86,7 @@ def load(path: str = LIB_PATH):
         "lq_gemv_workspace_bytes": ([], sz),
         "lq_gemv": ([i32, vp, vp, i32, vp, i64, i64, vp, sz, vp], i32),
         "lq_gemv_batch": ([ctypes.POINTER(lq_gemv_desc), i32, vp, sz, vp], i32),
+        "lq_gemv_batch_noalloc": ([ctypes.POINTER(lq_gemv_desc), i32, vp], i32),
         "lq_gemv_multi": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_gemv_multi_batch": ([ctypes.POINTER(lq_gemv_multi_desc), i32, vp, sz, vp], i32),
         "lq_gemm_workspace_bytes": ([i32, i64, i64, i64], sz),
@@ -230,6 +232,14 @@ def lq_gemv_batch(descs, ws=None, ws_bytes=None, stream=None):
     for i, (fmt, W, x, y, N, K) in enumerate(descs):
         arr[i] = lq_gemv_desc(_fmt(fmt), _xdt(x), _ptr(W), _ptr(x), _ptr(y), N, K)
     _check(load().lq_gemv_batch(arr, len(descs), _ptr(ws), _ws_bytes(ws, ws_bytes), _stream(stream)))
+
+
+def lq_gemv_batch_noalloc(descs, stream=None):
+    """lq_gemv_batch with the library's static workspace (allocates nothing)."""
+    arr = (lq_gemv_desc * max(1, len(descs)))()
+    for i, (fmt, W, x, y, N, K) in enumerate(descs):
+        arr[i] = lq_gemv_desc(_fmt(fmt), _xdt(x), _ptr(W), _ptr(x), _ptr(y), N, K)
+    _check(load().lq_gemv_batch_noalloc(arr, len(descs), _stream(stream)))
 
 
 def lq_gemv_multi(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=None, stream=None, xdt=None):

@@ -11,6 +11,13 @@
 #include <mutex>
 #include <vector>
 
+// Split-K workspace of lq_gemv_batch_noalloc, for callers that cannot
+// allocate: part of the library's code object, one copy per device (the GPU
+// holds it until the process ends).  Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol): it takes the
+// device address from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[lq::kGemvWorkspaceBytes];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -353,6 +360,27 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
     return e == hipSuccess ? LQ_OK : hip_fail(e, "multi-token GEMV launch");
 }
 
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// Device address of this device's `scratch` (looked up on first use).
+lq_status scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(LQ_ERR_HIP, "device index %d unsupported", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(LQ_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LQ_OK;
+}
+
 }  // namespace
 
 namespace lq {
@@ -379,7 +407,9 @@ lq_status lq_init(void) {
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
     if (n < 1) return fail(LQ_ERR_HIP, "no HIP device present");
     int cus = 0;
-    return device_cus(&cus);
+    LQ_TRY(device_cus(&cus));
+    void* p = nullptr;
+    return scratch_ptr(&p);
 }
 
 int32_t lq_block_elems(int32_t fmt) { return block_of(fmt); }
@@ -477,6 +507,19 @@ lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* ws, size
         if (!chunk.empty()) LQ_TRY(launch_chunk(descs[i].fmt, descs[i].xdt, 1, chunk, cus, w, st));
     }
     return LQ_OK;
+}
+
+lq_status lq_gemv_batch_noalloc(const lq_gemv_desc* descs, int32_t count, void* stream) {
+    // Validate everything before the first HIP call, as lq_gemv_batch does;
+    // its workspace is this device's `scratch`, which always has the size a
+    // GEMV workspace needs (the launch planner splits K only within it).
+    if (!descs) return fail(LQ_ERR_ARG, "descs is NULL");
+    if (count < 1) return fail(LQ_ERR_ARG, "count=%d must be >= 1", count);
+    for (int32_t i = 0; i < count; ++i) LQ_TRY(check_gemv_desc(descs[i], i));
+    static_assert(sizeof(scratch) >= lq::kGemvWorkspaceBytes, "scratch holds a GEMV workspace");
+    void* p = nullptr;
+    LQ_TRY(scratch_ptr(&p));
+    return lq_gemv_batch(descs, count, p, sizeof(scratch), stream);
 }
 
 lq_status lq_gemv(int32_t fmt, const void* W, const void* x, int32_t xdt, float* y, int64_t N,

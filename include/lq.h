@@ -235,6 +235,18 @@ typedef struct lq_gemv_desc {
 lq_status lq_gemv_batch(const lq_gemv_desc* descs, int32_t count, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* lq_gemv_batch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and results as lq_gemv_batch with a workspace, but the
+ * workspace is a static array inside the library (lq_gemv_workspace_bytes()
+ * bytes, 4.5 MiB, one per device, held until the process ends); nothing is
+ * allocated.  That array needs no clearing, but every call on a device
+ * shares it: calls that overlap in time on one device (unordered streams,
+ * several threads) race and give wrong results.  Calls on one stream are
+ * safe.  Every launch fits the array (K is split only within it), so no
+ * shape is rejected for its size. */
+lq_status lq_gemv_batch_noalloc(const lq_gemv_desc* descs, int32_t count, void* stream);
+
 /* Multi-token GEMV, the decode step of a few tokens at once (verification of
  * drafted tokens: "oxinfer" page, "Speculative decoding", and the multi-token
  * variants of its decode kernels in "How it works"):

@@ -98,6 +98,10 @@ def test_rejections_before_any_hip_call(L):
     assert g.lq_gemv_batch(d, 2, A16 + 8, wsb, None) == ALIGN
     assert g.lq_gemv(0, A16, A16, 0, A16, 4, 32, A16, 64, None) == WS
     assert g.lq_gemv_multi(0, A16, A16, 1, A16, 4, 64, 32, A16, 16, None) == WS
+    assert g.lq_gemv_batch_noalloc(None, 1, None) == ARG
+    assert g.lq_gemv_batch_noalloc(d, 0, None) == ARG
+    d[1] = lq.lq_gemv_desc(0, 0, A16, A16, A16, 4, 40)
+    assert g.lq_gemv_batch_noalloc(d, 2, None) == SHAPE
     # gemm
     assert g.lq_gemm(0, A16, A16, 0, A16, 16, 32, 32, None, 0, None) == UNSUP     # fp32 X
     assert g.lq_gemm(2, A16, A16, 1, A16, 16, 32, 32, None, 0, None) == SHAPE     # int8 block 64
