@@ -432,6 +432,321 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
         }
 }
 
+// ------------------------------------------------------------------------
+// Wave-fragment GEMM for the fp16-scale formats (Q4_0, Q8_0).
+//
+// A workgroup of 4 waves, one per SIMD, owns a (64 MI) x (64 NJ) output tile;
+// wave (wm, wn) owns rows 32 MI wm .. +32 MI and columns 32 NJ wn .. +32 NJ,
+// MI x NJ blocks of 32 x 32 fp32 accumulators (accumulation registers).  The
+// copy ring (global_load_lds, straight to LDS) carries the step's X tile and
+// the raw codes and scales of the workgroup's NJ packed 64-row tiles, D - 2
+// steps ahead of use.  Each wave decodes the weight fragments it multiplies
+// itself, in registers, from the raw codes in LDS: lane (c, h) of block j
+// takes bytes 8h .. 8h + 7 of column c's block, whose low nibbles (Q4_0) or
+// first code part (Q8_0) are elements 8h .. 8h + 7 of the first 16-element
+// half of the block and whose high nibbles / second part are elements
+// 16 + 8h .. of the second, exactly the B operand layout of
+// v_mfma_f32_32x32x16_f16.  No decoded tile is written back to LDS, and the
+// one barrier per step only guards the ring.  A wave's vector work (decode,
+// fragment reads, copy issue) runs while its own matrix instructions execute
+// (measured: a wave per SIMD issuing 24 of them and ~130 decode-like vector
+// ops per step runs at the matrix-only rate), so the step costs its matrix
+// time: the MFMAs of step st use fragments prepared during step st - 1.
+
+template <int FMT, int MI, int NJ>
+struct WCfg {
+    static constexpr int P = FMT == kQ4_0 ? 1 : 2;
+    static constexpr int BM = 64 * MI;
+    static constexpr int BN = 64 * NJ;
+    static constexpr int NT = NJ;                          // packed 64-row tiles per workgroup
+    static constexpr int kXBytes = BM * kXRowBytes;
+    static constexpr int kWOff = kXBytes;
+    static constexpr int kSOff = kWOff + NT * P * 1024;
+    static constexpr int kSlotBytes = kSOff + NT * 256;
+    // Behind the ring: where the copies of waves with nothing to copy land
+    // (1 KB for a code copy, 256 B for a scale copy); nothing reads it.
+    static constexpr int kDummyBytes = 1024 + 256;
+    static constexpr int kStages =
+        (160 * 1024 - kDummyBytes) / kSlotBytes > 8 ? 8 : (160 * 1024 - kDummyBytes) / kSlotBytes;
+    static constexpr int kDummyOff = kStages * kSlotBytes;
+    static constexpr int kLdsBytes = kDummyOff + kDummyBytes;
+    static constexpr int kXLoads = BM / 16;                // 1 KB copies of X per step
+    static constexpr int kXPerWave = kXLoads / 4;
+    static constexpr int kCodePerWave = (NT * P + 3) / 4;  // 16-byte code copies (wave w: parts w + 4 k)
+    static constexpr int kScalePerWave = (NT + 3) / 4;     // 2-byte scale copies
+    static constexpr int kLoadsPerStep = kXPerWave + kCodePerWave + kScalePerWave;
+    static_assert(kXLoads % 4 == 0, "X copies split evenly");
+    static_assert(kStages >= 4, "ring depth");
+    static_assert((kStages - 2) * kLoadsPerStep <= 63, "vmcnt range");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
+
+template <int FMT, int MI, int NJ>
+__global__ __launch_bounds__(256, 1) void gemm_wave_kernel(const GemmArgs a) {
+    using C = WCfg<FMT, MI, NJ>;
+    constexpr int P = C::P;
+    constexpr int D = C::kStages;
+    constexpr int L = C::kLoadsPerStep;
+    constexpr int NT = C::NT;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    int Lw = blockIdx.x;
+    if (a.remap) Lw = (Lw % 8) * int(gridDim.x / 8) + Lw / 8;
+    int mi = 0;
+    for (int i = 1; i < a.count; ++i) mi += Lw >= a.mat[i].wg0 ? 1 : 0;
+    const GemmMat& G = a.mat[mi];
+    const int local = Lw - G.wg0;
+    const int tm = local % a.tiles_m;
+    const int rest = local / a.tiles_m;
+    const int tn = rest % G.tiles_n;
+    const int ks = rest / G.tiles_n;
+    const int m0 = tm * C::BM;
+    const int u0 = ks * a.us;
+    const int nst = min(a.nu, u0 + a.us) - u0;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int c = lane & 31, h = lane >> 5;
+    const int tiles_b = (G.N + kTileRows - 1) / kTileRows;
+
+    // ---- copy ring: kXPerWave X copies (rows 16 (4 k + ... ) of the tile),
+    // then kOthers code / scale / spare copies, numbered q = wave + 4 k.
+    size_t xo[C::kXPerWave];
+#pragma unroll
+    for (int i = 0; i < C::kXPerWave; ++i) {
+        const int row = 16 * (C::kXPerWave * wave + i) + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 2) & 3);
+        xo[i] = size_t(min(m0 + row, a.M - 1)) * size_t(a.K) * 2u + size_t(ch) * 16u;
+    }
+    // Code copy k of wave w carries part q = w + 4 k (packed tile q / P,
+    // code part q % P) and scale copy k the scales of packed tile w + 4 k;
+    // copies past the last real one go to the dummy area.  Every wave issues
+    // the same copies of each kind, so the copy code has no branch.
+    const uint8_t* csrc[C::kCodePerWave];
+    uint32_t cstep[C::kCodePerWave], cdst[C::kCodePerWave];
+#pragma unroll
+    for (int k = 0; k < C::kCodePerWave; ++k) {
+        const int q = wave + 4 * k;
+        const bool real = q < NT * P;
+        const int t = real ? q / P : 0;
+        const int ltb = min(tn * NT + t, tiles_b - 1);
+        const int lnr = min(kTileRows, G.N - ltb * kTileRows);
+        const uint32_t lrow = uint32_t(min(lane, lnr - 1));
+        csrc[k] = G.codes + size_t(ltb) * kTileRows * size_t(a.nu) * P * 16 +
+                  (size_t(u0) * P + size_t(real ? q % P : 0)) * size_t(lnr) * 16 + lrow * 16;
+        cstep[k] = uint32_t(P * lnr * 16);
+        cdst[k] = real ? uint32_t(C::kWOff + q * 1024) : ~0u;
+    }
+    const uint8_t* ssrc[C::kScalePerWave];
+    uint32_t sstep[C::kScalePerWave], sdst[C::kScalePerWave];
+#pragma unroll
+    for (int k = 0; k < C::kScalePerWave; ++k) {
+        const int t0 = wave + 4 * k;
+        const bool real = t0 < NT;
+        const int t = real ? t0 : 0;
+        const int ltb = min(tn * NT + t, tiles_b - 1);
+        const int lnr = min(kTileRows, G.N - ltb * kTileRows);
+        const uint32_t lrow = uint32_t(min(lane, lnr - 1));
+        ssrc[k] = G.scales + (size_t(ltb) * kTileRows * size_t(a.nu) + size_t(u0) * lnr + lrow) * 2;
+        sstep[k] = uint32_t(lnr * 2);
+        sdst[k] = real ? uint32_t(C::kSOff + t * 256) : ~0u;
+    }
+    auto slot_of = [&](int st) { return lds + (st % D) * C::kSlotBytes; };
+    // Copy n (0 .. L - 1) of step st: X copies, then code copies, then scale
+    // copies (n is a compile-time index after unrolling).
+    auto issue_one = [&](int st, int n) {
+        uint8_t* slot = slot_of(st);
+        if (n < C::kXPerWave) {
+            const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.X) + size_t(u0 + st) * 64;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(xb + xo[n]),
+                (__attribute__((address_space(3))) void*)(slot + (C::kXPerWave * wave + n) * 1024), 16, 0, 0);
+        } else if (n < C::kXPerWave + C::kCodePerWave) {
+            const int k = n - C::kXPerWave;
+            uint8_t* dst = cdst[k] == ~0u ? lds + C::kDummyOff : slot + cdst[k];
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(csrc[k] + size_t(st) * cstep[k]),
+                (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        } else {
+            const int k = n - C::kXPerWave - C::kCodePerWave;
+            uint8_t* dst = sdst[k] == ~0u ? lds + C::kDummyOff + 1024 : slot + sdst[k];
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(ssrc[k] + size_t(st) * sstep[k]),
+                (__attribute__((address_space(3))) void*)dst, 2, 0, 0);
+        }
+    };
+    auto issue = [&](int st) {
+#pragma unroll
+        for (int n = 0; n < L; ++n) issue_one(st, n);
+    };
+
+    // ---- fragments.  A: lane (c, h) of block i, half s: X row
+    // 32 MI wm + 32 i + c, elements 16 s + 8 h .. + 7 (chunk 2 s + h).
+    // B: block j is the wave's block wn NJ + j of the workgroup's columns:
+    // packed tile (wn NJ + j) / 2, rows 32 ((wn NJ + j) % 2) + c.
+    uint32_t a_off[2], b_code[NJ], b_scale[NJ];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) a_off[s] = sw_off(32 * MI * wm + c, 2 * s + h);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int bj = wn * NJ + j;
+        const int rr = 32 * (bj & 1) + c;
+        b_code[j] = uint32_t(C::kWOff + (bj >> 1) * P * 1024 + rr * 16 + 8 * h);
+        b_scale[j] = uint32_t(C::kSOff + (bj >> 1) * 256 + rr * 4);
+    }
+    f32x16 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Fragments of a step: A[s][i], B[s][j] for the two 16-element halves s
+    // (B as the four dwords of the 8 fp16 weights).
+    struct Frags {
+        half8_t a[2][MI];
+        u32x4 b[2][NJ];
+    };
+    // Raw codes and scale of block j, and the decoded dwords: dword e of half
+    // s is the weight pair (8h + 2e, 8h + 2e + 1) of that half.
+    struct Raw {
+        u32x2 cw[NJ][P];
+        uint32_t dv[NJ];
+    };
+    auto read_raw = [&](const uint8_t* slot, Raw& r) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) r.cw[j][p] = *reinterpret_cast<const u32x2*>(slot + b_code[j] + p * 1024);
+            r.dv[j] = *reinterpret_cast<const uint16_t*>(slot + b_scale[j]);
+        }
+    };
+    auto read_a = [&](const uint8_t* slot, Frags& f) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < MI; ++i) f.a[s][i] = *reinterpret_cast<const half8_t*>(slot + a_off[s] + i * 2048);
+    };
+    // Pair e (0..3) of half s of block j.  Q4_0: the low nibbles of the 8
+    // code bytes are half 0, the high nibbles half 1; Q8_0: code part s.
+    auto decode = [&](const Raw& r, int j, int s, int e) -> uint32_t {
+        const _Float16 dh = __builtin_bit_cast(_Float16, uint16_t(r.dv[j]));
+        const half2_t dd = {dh, dh};
+        const uint32_t sel = (e & 1) ? 0x04030402u : 0x04010400u;
+        if constexpr (P == 1) {
+            const uint32_t w = (e & 2) ? r.cw[j][0].y : r.cw[j][0].x;
+            const uint32_t n = (s ? (w >> 4) : w) & 0x0F0F0F0Fu;
+            return w2(n, sel, dd);
+        } else {
+            const uint32_t w = ((e & 2) ? r.cw[j][s].y : r.cw[j][s].x) ^ 0x80808080u;
+            return w8(w, sel, dd);
+        }
+    };
+    auto mfma = [&](const Frags& f, int g) {
+        const int s = g / (MI * NJ), i = (g / NJ) % MI, j = g % NJ;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[s][i], __builtin_bit_cast(half8_t, f.b[s][j]),
+                                                           acc[i][j], 0, 0, 0);
+    };
+
+    // One step: the matrix instructions of step st on `cur`, one at a time,
+    // each followed by a slice of the work for step st + 1: first the raw
+    // code and scale reads, then one copy of step st + D - 1 per slice, then
+    // two decoded weight pairs per slice (the A fragment reads of step st + 1
+    // go behind the first of those, whose wait for the raw codes would
+    // otherwise also wait for them).  This work issues while the matrix core
+    // runs; sched_barrier(0) keeps the compiler from regrouping the slices.
+    constexpr int kMfma = 2 * MI * NJ;
+    constexpr int kPairs = 8 * NJ;
+    constexpr int kFirstDec = 1 + L;
+    static_assert(kFirstDec + kPairs / 2 <= kMfma, "slices");
+    auto step = [&](int st, const Frags& cur, Frags& nxt) {
+        // Step st + 1 has landed for every wave, and every wave is done with
+        // step st - 1, whose slot the copies below may now refill.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 3) * L));
+        lds_barrier();
+        const uint8_t* slot = slot_of(st + 1);            // past the last step: unused data
+        const int cst = min(st + D - 1, nst - 1);
+        Raw raw;
+#pragma unroll
+        for (int g = 0; g < kMfma; ++g) {
+            mfma(cur, g);
+            __builtin_amdgcn_sched_barrier(0);
+            if (g == 0) {
+                read_raw(slot, raw);
+            } else if (g < kFirstDec) {
+                issue_one(cst, g - 1);
+            } else if (g < kFirstDec + kPairs / 2) {
+#pragma unroll
+                for (int q = 2 * (g - kFirstDec); q < 2 * (g - kFirstDec) + 2; ++q) {
+                    const int j = q / 8, s = (q / 4) & 1, e = q & 3;
+                    nxt.b[s][j][e] = decode(raw, j, s, e);
+                }
+                if (g == kFirstDec) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_a(slot, nxt);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (nst > 0) {
+        Frags f0, f1;
+#pragma unroll
+        for (int p = 0; p < D - 1; ++p) issue(min(p, nst - 1));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 2) * L));   // step 0 landed
+        lds_barrier();
+        {
+            Raw raw;
+            read_raw(slot_of(0), raw);
+            read_a(slot_of(0), f0);
+#pragma unroll
+            for (int q = 0; q < kPairs; ++q) f0.b[(q / 4) & 1][q / 8][q & 3] = decode(raw, q / 8, (q / 4) & 1, q & 3);
+        }
+        int st = 0;
+        for (; st + 1 < nst; st += 2) {
+            step(st, f0, f1);
+            step(st + 1, f1, f0);
+        }
+        if (st < nst) step(st, f0, f1);
+    }
+
+    // ---- epilogue: straight from the accumulators (register r of lane l is
+    // row 8 (r / 4) + 4 (l / 32) + r % 4 of the block, column l % 32).
+    // A wave whose rows and columns all exist stores without checks: the row
+    // part of each address is wave-uniform, the lane part fixed.
+    float* out = G.out + size_t(ks) * size_t(a.M) * size_t(G.N);
+    const int n0 = tn * C::BN + 32 * NJ * wn;
+    const int r0 = m0 + 32 * MI * wm;
+    const size_t lane_off = size_t(4 * h) * size_t(G.N) + size_t(c);
+    if (r0 + 32 * MI <= a.M && n0 + 32 * NJ <= G.N) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float* rowp = out + size_t(r0 + 32 * i + 8 * (r / 4) + (r % 4)) * size_t(G.N) + (n0 + 32 * j);
+                    rowp[lane_off] = acc[i][j][r];
+                }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = n0 + 32 * j + c;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+                if (row < a.M && col < G.N) out[size_t(row) * size_t(G.N) + col] = acc[i][j][r];
+            }
+        }
+}
+
 // Y = sum of the S partial slices, added in slice order.
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P, float* __restrict__ Y,
                                                      size_t mn, int S) {
@@ -514,6 +829,24 @@ hipError_t launch_tile(const GemmArgs& a, int64_t grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int FMT, int NJ>
+hipError_t launch_wave(const GemmArgs& a, int64_t grid, hipStream_t stream) {
+    using C = WCfg<FMT, 4, NJ>;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static std::atomic<bool> lds_ok[64];
+    if (!lds_ok[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wave_kernel<FMT, 4, NJ>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+        if (e != hipSuccess) return e;
+        lds_ok[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL((gemm_wave_kernel<FMT, 4, NJ>), dim3(unsigned(grid)), dim3(256), C::kLdsBytes, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
@@ -561,8 +894,13 @@ hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, cons
     a.us = p.us;
     a.remap = (wgs % 8 == 0) ? 1 : 0;
     hipError_t e;
+#ifdef LQ_GEMM_TILE_ONLY
     if (fmt == kQ4_0) e = p.nt == 3 ? launch_tile<kQ4_0, 3>(a, wgs, stream) : launch_tile<kQ4_0, 2>(a, wgs, stream);
     else if (fmt == kQ8_0) e = p.nt == 3 ? launch_tile<kQ8_0, 3>(a, wgs, stream) : launch_tile<kQ8_0, 2>(a, wgs, stream);
+#else
+    if (fmt == kQ4_0) e = p.nt == 3 ? launch_wave<kQ4_0, 3>(a, wgs, stream) : launch_wave<kQ4_0, 2>(a, wgs, stream);
+    else if (fmt == kQ8_0) e = p.nt == 3 ? launch_wave<kQ8_0, 3>(a, wgs, stream) : launch_wave<kQ8_0, 2>(a, wgs, stream);
+#endif
     else if (fmt == kI8B64) e = launch_tile<kI8B64, 2>(a, wgs, stream);
     else e = launch_tile<kI8B32, 2>(a, wgs, stream);
     if (e != hipSuccess || p.S == 1) return e;
