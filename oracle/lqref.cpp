@@ -324,6 +324,78 @@ int lqref_quantize(int fmt, const void* src, int sdt, int64_t N, int64_t K,
     return 0;
 }
 
+int lqref_quantize_act(const void* X, int xdt, int64_t M, int64_t K,
+                       int8_t* q, float* s, int32_t* sum) {
+    if (!X || !q || !s || !sum || M < 0 || K < 0 || K % 32 != 0) return -1;
+    if (xdt != LQREF_F32 && xdt != LQREF_F16) return -1;
+    const int64_t nb = K / 32;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float x[32];
+            for (int e = 0; e < 32; ++e) x[e] = source_at(X, xdt, m * K + b * 32 + e);
+            float a = 0.0f;
+            for (int e = 0; e < 32; ++e) a = std::fabs(x[e]) > a ? std::fabs(x[e]) : a;
+            const float sc = a / 127.0f;
+            int32_t t = 0;
+            for (int e = 0; e < 32; ++e) {
+                const int c = sc == 0.0f ? 0 : round_clamp(x[e] / sc, -127, 127);
+                q[m * K + b * 32 + e] = int8_t(c);
+                t += c;
+            }
+            s[m * nb + b] = sc;
+            sum[m * nb + b] = t;
+        }
+    }
+    return 0;
+}
+
+// Integer code and scale of the weight block of row n that holds element k:
+// Q4_0 q - 8 with the fp16 d, Q8_0 the int8 code with the fp16 d, the int8
+// formats the code with the fp32 scale of its 64- or 32-block.
+static void code_and_scale(int fmt, const uint8_t* w, const void* scales, int64_t K, int64_t n, int64_t k,
+                           int* code, double* scale) {
+    if (planar(fmt)) {
+        const int64_t E = block_elems(fmt);
+        *code = reinterpret_cast<const int8_t*>(w)[n * K + k];
+        *scale = static_cast<const float*>(scales)[n * (K / E) + k / E];
+        return;
+    }
+    const int bb = gguf_block_bytes(fmt);
+    const uint8_t* blk = w + (n * (K / 32) + k / 32) * bb;
+    *scale = half_to_double(static_cast<uint16_t>(blk[0] | (blk[1] << 8)));
+    const int j = int(k % 32);
+    if (fmt == LQREF_Q4_0) *code = (j < 16 ? (blk[2 + j] & 0x0F) : (blk[2 + j - 16] >> 4)) - 8;
+    else *code = static_cast<int8_t>(blk[2 + j]);
+}
+
+int lqref_gemv_q8act(int fmt, const uint8_t* w, const void* scales,
+                     const int8_t* q, const float* s, int64_t M, int64_t N, int64_t K,
+                     double* Y, double* S, int nthreads) {
+    if (!shape_ok(fmt, N, K) || !w || !q || !s || !Y || !S || M < 0) return -1;
+    if (planar(fmt) && !scales) return -1;
+    const int64_t nb = K / 32;
+    parallel_for(N, nthreads, [&](int64_t n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, abs_acc = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                int64_t I = 0;
+                double ws = 0.0;
+                for (int e = 0; e < 32; ++e) {
+                    int c;
+                    code_and_scale(fmt, w, scales, K, n, b * 32 + e, &c, &ws);
+                    I += int64_t(c) * int64_t(q[m * K + b * 32 + e]);
+                }
+                const double t = ws * static_cast<double>(s[m * nb + b]) * static_cast<double>(I);
+                acc += t;
+                abs_acc += std::fabs(t);
+            }
+            Y[m * N + n] = acc;
+            S[m * N + n] = abs_acc;
+        }
+    });
+    return 0;
+}
+
 int lqref_gemv(int fmt, const uint8_t* w, const void* scales, const void* x,
                int xdt, int64_t N, int64_t K, const int64_t* rows, int64_t nrows,
                double* y, double* S, int nthreads) {

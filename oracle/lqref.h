@@ -96,6 +96,31 @@ int lqref_gemm(int fmt, const uint8_t* w, const void* scales,
                const int64_t* ms, int64_t nm, const int64_t* ns, int64_t nn,
                int round_w_f16, double* Y, double* S, int nthreads);
 
+/* Per-matmul activation quantization ("oxinfer" page, "How it works",
+ * quant.rs: activations are quantized for each matmul and the decode kernels
+ * take integer dot products of int8 activations with the weight codes).  The
+ * page gives no rule; the reading here is the page's own Q8 rule (32 values
+ * per fp32 scale) applied to each 32-element block of each token row of X
+ * (M x K, fp32 or fp16 bits), in IEEE fp32 operations:
+ *   a = max |x| over the block; s = a / 127 (fp32);
+ *   q = clamp(rint(x / s), -127, 127) (rint: nearest, ties to even), 0 when s == 0;
+ *   sum = the block's sum of q (int32).
+ * Outputs: q (M*K int8), s (M*K/32 fp32), sum (M*K/32 int32). */
+int lqref_quantize_act(const void* X, int xdt, int64_t M, int64_t K,
+                       int8_t* q, float* s, int32_t* sum);
+
+/* Integer-dot product on quantized activations (q, s as above):
+ *   Y[m,n] = sum_b  ws(n,b) * s[m,b] * I(m,n,b),
+ *   I(m,n,b) = sum over the 32 elements k of block b of c(n,k) * q[m,k],
+ * where c is the weight's integer code (q - 8 for Q4_0, the int8 code
+ * otherwise) and ws(n,b) the scale of the weight block holding block b (fp16
+ * d, or the fp32 scale; an int8 block-64 scale covers two blocks).  I is
+ * exact; the sum over b is in double.  S[m,n] = sum_b |ws s I|.  Output M x N
+ * row-major; K a multiple of the weight block. */
+int lqref_gemv_q8act(int fmt, const uint8_t* w, const void* scales,
+                     const int8_t* q, const float* s, int64_t M, int64_t N, int64_t K,
+                     double* Y, double* S, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ def _bind(L):
     L.lqref_unpack_gguf.argtypes = [i32, vp, i64, i64, vp, vp]
     L.lqref_quantize.argtypes = [i32, vp, i32, i64, i64, vp, vp]
     L.lqref_gemv.argtypes = [i32, vp, vp, vp, i32, i64, i64, vp, i64, vp, vp, i32]
+    L.lqref_quantize_act.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    L.lqref_gemv_q8act.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, vp, vp, i32]
     L.lqref_gemm.argtypes = [i32, vp, vp, vp, i32, i64, i64, i64,
                              vp, i64, vp, i64, i32, vp, vp, i32]
     return L
@@ -134,6 +136,27 @@ class Oracle:
         scales = np.empty((N, K // 32), np.uint16)
         _check(self.L.lqref_unpack_gguf(fmt, _p(aos), N, K, _p(codes), _p(scales)), "unpack_gguf")
         return codes, scales
+
+    def quantize_act(self, X, M, K):
+        """Per-matmul activation quantization of M x K activations (float32
+        or float16): returns (q int8 M x K, s fp32 M x K/32, sum int32 M x K/32)."""
+        xdt, xa = _xdt(np.asarray(X).reshape(-1))
+        q = np.empty((M, K), np.int8)
+        s = np.empty((M, K // 32), np.float32)
+        t = np.empty((M, K // 32), np.int32)
+        _check(self.L.lqref_quantize_act(_p(xa), xdt, M, K, _p(q), _p(s), _p(t)), "quantize_act")
+        return q, s, t
+
+    def gemv_q8act(self, fmt, w, scales, q, s, M, N, K, nthreads=None):
+        """Integer-dot product on quantized activations: (Y, S) in float64, M x N."""
+        q = np.ascontiguousarray(q, np.int8)
+        s = np.ascontiguousarray(s, np.float32)
+        Y = np.empty((M, N), np.float64)
+        S = np.empty((M, N), np.float64)
+        nt = nthreads or os.cpu_count() or 1
+        _check(self.L.lqref_gemv_q8act(fmt, _p(w), _p(scales), _p(q), _p(s), M, N, K, _p(Y), _p(S), nt),
+               "gemv_q8act")
+        return Y, S
 
     def gemv(self, fmt, w, scales, x, N, K, rows=None, nthreads=None):
         """Returns (y, S) in float64 for the selected rows (all rows by default)."""

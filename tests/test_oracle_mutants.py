@@ -7,6 +7,7 @@ import pytest
 from oracle import lqref
 from tests.test_oracle_pins import ALL_PINS
 from tests.test_oracle_quant import QUANT_PINS
+from tests.test_oracle_q8act import Q8ACT_PINS
 
 MUTANTS = {
     # nibble order (2j, 2j+1) instead of (j, j+16)
@@ -47,6 +48,25 @@ MUTANTS = {
     # quantizer: int8 block-64 maximum over the first half of the block only
     "quant_i8_half_block": ("for (int e = 0; e < E; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;\n                const float s",
                             "for (int e = 0; e < 32; ++e) a = std::fabs(w[e]) > a ? std::fabs(w[e]) : a;\n                const float s"),
+    # activation quantizer: divisor 128
+    "act_divisor": ("const float sc = a / 127.0f;", "const float sc = a / 128.0f;"),
+    # activation quantizer: block sum of |q|
+    "act_sum_abs": ("            t += c;", "            t += c < 0 ? -c : c;"),
+    # activation quantizer: the largest element from the first half block only
+    "act_half_block": ("for (int e = 0; e < 32; ++e) a = std::fabs(x[e]) > a ? std::fabs(x[e]) : a;\n            const float sc",
+                       "for (int e = 0; e < 16; ++e) a = std::fabs(x[e]) > a ? std::fabs(x[e]) : a;\n            const float sc"),
+    # integer-dot product: Q4_0 offset dropped
+    "q8act_q4_offset": ("(blk[2 + j - 16] >> 4)) - 8;", "(blk[2 + j - 16] >> 4));"),
+    # integer-dot product: high nibble read as the low one
+    "q8act_high_nibble": ("(blk[2 + j - 16] >> 4)) - 8;", "(blk[2 + j - 16] & 0x0F)) - 8;"),
+    # integer-dot product: int8 block-64 scale indexed per 32 elements
+    "q8act_i8_scale_index": ("*scale = static_cast<const float*>(scales)[n * (K / E) + k / E];",
+                             "*scale = static_cast<const float*>(scales)[n * (K / E) + (k / 32) % (K / E)];"),
+    # integer-dot product: every token uses token 0's codes
+    "q8act_token_row": ("I += int64_t(c) * int64_t(q[m * K + b * 32 + e]);", "I += int64_t(c) * int64_t(q[b * 32 + e]);"),
+    # integer-dot product: S without the absolute value
+    "q8act_abs": ("abs_acc += std::fabs(t);\n            }\n            Y[m * N + n] = acc;",
+                  "abs_acc += t;\n            }\n            Y[m * N + n] = acc;"),
     # quantizer: bf16 widened with the wrong shift
     "quant_bf16_shift": ("uint32_t bits = uint32_t(h) << 16;", "uint32_t bits = uint32_t(h) << 15;"),
 }
@@ -59,7 +79,7 @@ def test_pins_catch_mutant(name, tmp_path):
     assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
     mutant = lqref.build_variant(src.replace(old, new), str(tmp_path))
     failed = []
-    for pin in ALL_PINS + QUANT_PINS:
+    for pin in ALL_PINS + QUANT_PINS + Q8ACT_PINS:
         try:
             pin(mutant)
         except (AssertionError, ValueError):
