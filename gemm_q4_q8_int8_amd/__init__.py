@@ -24,7 +24,7 @@ EXPORTS = ("lq_abi_version", "lq_init", "lq_block_elems", "lq_packed_bytes", "lq
            "lq_gguf_bytes", "lq_repack_gguf", "lq_pack_planes", "lq_quantize", "lq_dequant_f32",
            "lq_dequant_f16", "lq_gemv_workspace_bytes", "lq_gemv", "lq_gemv_batch",
            "lq_gemv_batch_noalloc", "lq_gemv_multi",
-           "lq_gemv_multi_batch", "lq_gemm_workspace_bytes",
+           "lq_gemv_multi_batch", "lq_quantize_act", "lq_gemv_q8act", "lq_gemm_workspace_bytes",
            "lq_gemm", "lq_gemm_batch",
            "lq_matmul", "lq_status_str", "lq_last_error")
 
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH):
         "lq_gemv_batch_noalloc": ([ctypes.POINTER(lq_gemv_desc), i32, vp], i32),
         "lq_gemv_multi": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_gemv_multi_batch": ([ctypes.POINTER(lq_gemv_multi_desc), i32, vp, sz, vp], i32),
+        "lq_quantize_act": ([vp, i32, i64, i64, vp, vp, vp, vp], i32),
+        "lq_gemv_q8act": ([i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_gemm_workspace_bytes": ([i32, i64, i64, i64], sz),
         "lq_gemm": ([i32, vp, vp, i32, vp, i64, i64, i64, vp, sz, vp], i32),
         "lq_gemm_batch": ([i32, vp, i32, i64, i64, ctypes.POINTER(lq_gemm_desc), i32, vp, sz, vp], i32),
@@ -255,6 +257,17 @@ def lq_gemv_multi_batch(descs, ws=None, ws_bytes=None, stream=None):
         arr[i] = lq_gemv_multi_desc(_fmt(fmt), _xdt(X), _ptr(W), _ptr(X), _ptr(Y), M, N, K)
     _check(load().lq_gemv_multi_batch(arr, len(descs), _ptr(ws), _ws_bytes(ws, ws_bytes),
                                       _stream(stream)))
+
+
+def lq_quantize_act(X, M, K, q, s, sum, stream=None, xdt=None):
+    """X: float32 / float16 (M x K); q: int8 (M x K); s: float32 and sum: int32 (M x K/32)."""
+    xdt = _xdt(X) if xdt is None else xdt
+    _check(load().lq_quantize_act(_ptr(X), xdt, M, K, _ptr(q), _ptr(s), _ptr(sum), _stream(stream)))
+
+
+def lq_gemv_q8act(fmt, W, q, s, sum, Y, M, N, K, ws=None, ws_bytes=None, stream=None):
+    _check(load().lq_gemv_q8act(_fmt(fmt), _ptr(W), _ptr(q), _ptr(s), _ptr(sum), _ptr(Y), M, N, K, _ptr(ws),
+                                _ws_bytes(ws, ws_bytes), _stream(stream)))
 
 
 def lq_gemm(fmt, W, X, Y, M, N, K, ws=None, ws_bytes=None, stream=None, xdt=None):

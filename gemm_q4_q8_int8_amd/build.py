@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblq.so")
-SOURCES = ["lq_api.hip", "lq_gemv.hip", "lq_multi.hip", "lq_convert.hip", "lq_gemm.hip"]
+SOURCES = ["lq_api.hip", "lq_gemv.hip", "lq_multi.hip", "lq_q8act.hip", "lq_convert.hip", "lq_gemm.hip"]
 ARCH = os.environ.get("LQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -593,6 +593,61 @@ lq_status lq_gemv_multi(int32_t fmt, const void* W, const void* X, int32_t xdt, 
     return lq_gemv_multi_batch(&d, 1, ws, ws_bytes, stream);
 }
 
+lq_status lq_quantize_act(const void* X, int32_t xdt, int64_t M, int64_t K, int8_t* q, float* s, int32_t* sum,
+                          void* stream) {
+    LQ_TRY(check_xdt(xdt));
+    if (M < 1 || M > kMaxDim) return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, 2^31-1]", (long long)M);
+    if (K < 1 || K > kMaxK || K % 32 != 0)
+        return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 32 in [32, 2^25]", (long long)K);
+    if (M * (K / 32) > (int64_t(1) << 31) - 256) return fail(LQ_ERR_SHAPE, "too many activation blocks");
+    LQ_TRY(check_ptr(X, 16, "X"));
+    LQ_TRY(check_ptr(q, 16, "q"));
+    LQ_TRY(check_ptr(s, 4, "s"));
+    LQ_TRY(check_ptr(sum, 4, "sum"));
+    const hipError_t e = lq::launch_quantize_act(xdt, X, M, K, q, s, sum, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "activation quantization launch");
+}
+
+lq_status lq_gemv_q8act(int32_t fmt, const void* W, const int8_t* q, const float* s, const int32_t* sum, float* Y,
+                        int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream) {
+    LQ_TRY(check_fmt_shape(fmt, N, K));
+    if (M < 1 || M > lq::kQ8ActMaxTokens)
+        return fail(LQ_ERR_SHAPE, "M=%lld out of range [1, %d]", (long long)M, lq::kQ8ActMaxTokens);
+    LQ_TRY(check_ptr(W, 16, "W"));
+    LQ_TRY(check_ptr(q, 16, "q"));
+    LQ_TRY(check_ptr(s, 4, "s"));
+    LQ_TRY(check_ptr(sum, 4, "sum"));
+    LQ_TRY(check_ptr(Y, 4, "Y"));
+    LQ_TRY(check_gemv_ws(ws, ws_bytes));
+    int cus = 0;
+    LQ_TRY(device_cus(&cus));
+    // The K split of the single-token GEMV, with M tokens of partials per row.
+    const int64_t tiles = (N + lq::kTileRows - 1) / lq::kTileRows;
+    const int64_t nu = K / lq::unit_elems(fmt);
+    std::vector<int64_t> S(1, 1);
+    split_k(lq::gemv_min_units(fmt), cus, {tiles}, {nu}, {M}, S);
+    const GemvWs w = gemv_ws(ws);
+    if (!w.cnt) S[0] = 1;
+    if (tiles * S[0] > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows");
+    lq::Q8ActArgs a = {};
+    a.codes = static_cast<const uint8_t*>(W);
+    a.scales = static_cast<const uint8_t*>(W) + lq::align256(lq::code_plane_bytes(fmt, N, K));
+    a.q = q;
+    a.s = s;
+    a.sum = sum;
+    a.y = Y;
+    a.part = S[0] > 1 ? w.part : nullptr;
+    a.cnt = S[0] > 1 ? w.cnt : nullptr;
+    a.tag = lq::next_splitk_tag();
+    a.N = int32_t(N);
+    a.nu = int32_t(nu);
+    a.tiles = int32_t(tiles);
+    a.S = int32_t(S[0]);
+    a.M = int32_t(M);
+    const hipError_t e = lq::launch_gemv_q8act(fmt, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LQ_OK : hip_fail(e, "activation-quantized GEMV launch");
+}
+
 namespace {
 size_t gemm_ws(int32_t fmt, int64_t M, int64_t N, int64_t K) { return lq::gemm_workspace_bytes(fmt, M, N, K); }
 }  // namespace

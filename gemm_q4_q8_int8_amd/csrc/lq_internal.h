@@ -205,6 +205,33 @@ struct MultiArgs {
 
 hipError_t launch_gemv_multi(int fmt, const MultiArgs& a, hipStream_t stream);
 
+// ------------------------------------- activation-quantized GEMV ----
+// Activations quantized per 32-element block to int8 codes q (M x K), fp32
+// scales s and code sums (M x K / 32 each); Y = sum over blocks of
+// (w_scale * s) * (integer block dot product).
+constexpr int kQ8ActMaxTokens = 16;
+
+struct Q8ActArgs {
+    const uint8_t* codes;   // code plane (tiled)
+    const uint8_t* scales;  // scale plane (tiled)
+    const int8_t* q;        // M x K activation codes, row-major
+    const float* s;         // M x K/32 activation scales
+    const int32_t* sum;     // M x K/32 code sums (Q4_0's offset of 8)
+    float* y;               // M x N outputs, row-major
+    float* part;            // split-K partials: S slices x M tokens x tiles * 64 floats (S > 1 only)
+    uint64_t* cnt;          // one arrival counter per tile (S > 1 only)
+    uint64_t tag;           // this launch's split-K tag (splitk_arrive)
+    int32_t N;              // rows
+    int32_t nu;             // units per row
+    int32_t tiles;          // ceil(N / 64)
+    int32_t S;              // K slices (workgroups per tile)
+    int32_t M;              // tokens, 1 .. kQ8ActMaxTokens
+    int32_t pad;
+};
+hipError_t launch_quantize_act(int xdt, const void* X, int64_t M, int64_t K, int8_t* q, float* s, int32_t* sum,
+                               hipStream_t stream);
+hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, hipStream_t stream);
+
 // ------------------------------------------------------- conversions ----
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,
                               hipStream_t stream);

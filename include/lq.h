@@ -98,7 +98,7 @@
 extern "C" {
 #endif
 
-#define LQ_ABI_VERSION 7
+#define LQ_ABI_VERSION 8
 
 typedef enum lq_fmt { LQ_Q4_0 = 0, LQ_Q8_0 = 1, LQ_I8B64 = 2, LQ_I8B32 = 3 } lq_fmt;
 /* Activation and source dtypes.  LQ_BF16 is accepted only as the source of
@@ -286,6 +286,45 @@ typedef struct lq_gemv_multi_desc {
  * lq_gemv_multi) takes a launch of its own.  ws / ws_bytes as in lq_gemv. */
 lq_status lq_gemv_multi_batch(const lq_gemv_multi_desc* descs, int32_t count, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* Activation quantization for the integer-dot GEMV below.  The "oxinfer"
+ * page quantizes each matmul's activations and takes int8 dot products of
+ * them with the quantized weights ("How it works", quant.rs); it gives no
+ * rounding rule, and the one here is its own Q8 rule ("How it works": 32
+ * weights per scale) applied to activations.  For each token m < M and each
+ * 32-element block b of its row, in fp32:
+ *   s[m, b]   = max |X[m, k]| over the block / 127
+ *   q[m, k]   = clamp(rint(X[m, k] / s[m, b]), -127, 127), rint rounding
+ *               half to even (all codes 0 when s[m, b] = 0)
+ *   sum[m, b] = sum of the block's 32 codes
+ * so that |X - q s| <= s / 2 elementwise.  X: M x K, dtype xdt (LQ_F32 or
+ * LQ_F16), row-major, 16-byte aligned, finite (a block holding an infinity
+ * or NaN gets unspecified codes and scale).  q: M x K int8, 16-byte aligned;
+ * s: M x K/32 fp32; sum: M x K/32 int32 (both 4-byte aligned; all row-major).
+ * M >= 1, K a multiple of 32 (K <= 2^25), M * K / 32 <= 2^31 - 256. */
+lq_status lq_quantize_act(const void* X, int32_t xdt, int64_t M, int64_t K,
+                          int8_t* q, float* s, int32_t* sum, void* stream);
+
+/* Activation-quantized decode GEMV for 1 <= M <= 16 tokens (the "oxinfer"
+ * page's int8 dot-product decode kernels, "How it works", quant.rs, with their
+ * multi-token variants for drafted tokens, "Speculative decoding"):
+ *   Y[m, n] = sum over blocks b of (ws[n, b] * s[m, b]) * I[m, n, b],
+ *   I[m, n, b] = sum over the block's 32 k of c[n, k] * q[m, k]  (exact int)
+ * with c the weight's integer code (Q4_0: stored nibble - 8; Q8_0 and the
+ * int8 formats: the int8 code), ws its block scale (LQ_I8B64's scale covers
+ * two activation blocks), and q, s, sum as lq_quantize_act writes them (sum
+ * is read for LQ_Q4_0 only, but must be valid for every format).  Every
+ * weight is read once for all M tokens.  The block sums I are exact (int8
+ * dot products with int32 accumulation); each is scaled by fl(ws * s) and
+ * accumulated in fp32.  Accuracy: |Y - Y_q| <= 1e-4 * sum_b |ws s I| + 1e-6
+ * per output, Y_q the exact value of the sum above.  W: packed N x K; q / s /
+ * sum: M tokens of K codes, K/32 scales and K/32 sums (alignment as in
+ * lq_quantize_act); Y: M x N fp32 row-major, 4-byte aligned.  ws / ws_bytes:
+ * a GEMV workspace or NULL / 0, as in lq_gemv.  M outside [1, 16] is
+ * LQ_ERR_SHAPE. */
+lq_status lq_gemv_q8act(int32_t fmt, const void* W, const int8_t* q, const float* s,
+                        const int32_t* sum, float* Y, int64_t M, int64_t N, int64_t K,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes lq_gemm needs for these arguments (0 means none): the fp32
  * partial products of K slices when the GEMM splits K across workgroups.

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_names(L):
-    assert lq.lq_abi_version() == 7
+    assert lq.lq_abi_version() == 8
     names = [lq.lq_status_str(s) for s in range(9)]
     assert names == ["LQ_OK", "LQ_ERR_ARG", "LQ_ERR_SHAPE", "LQ_ERR_ALIGN", "LQ_ERR_FMT",
                      "LQ_ERR_DTYPE", "LQ_ERR_UNSUPPORTED", "LQ_ERR_WORKSPACE", "LQ_ERR_HIP"]
@@ -145,6 +145,27 @@ def test_rejections_before_any_hip_call(L):
     md[1] = lq.lq_gemv_multi_desc(1, 0, A16, A16, A16, 4, 64, 32)
     assert g.lq_gemv_multi_batch(md, 2, None, 0, None) == UNSUP          # fp32 activations
     assert "descriptor 1" in lq.lq_last_error()
+    # activation quantization: K a multiple of 32, q 16-byte aligned, s / sum 4-byte
+    assert g.lq_quantize_act(A16, 2, 2, 64, A16, A16, A16, None) == DTYPE
+    assert g.lq_quantize_act(A16, 0, 0, 64, A16, A16, A16, None) == SHAPE
+    assert g.lq_quantize_act(A16, 0, 2, 48, A16, A16, A16, None) == SHAPE
+    assert g.lq_quantize_act(A16, 0, 2, 2 ** 25 + 32, A16, A16, A16, None) == SHAPE
+    assert g.lq_quantize_act(A16, 0, 2 ** 22, 2 ** 14, A16, A16, A16, None) == SHAPE   # 2^31 blocks
+    assert g.lq_quantize_act(A16 + 4, 0, 2, 64, A16, A16, A16, None) == ALIGN
+    assert g.lq_quantize_act(A16, 0, 2, 64, A16 + 4, A16, A16, None) == ALIGN
+    assert g.lq_quantize_act(A16, 0, 2, 64, A16, A16 + 2, A16, None) == ALIGN
+    assert g.lq_quantize_act(A16, 0, 2, 64, A16, A16, None, None) == ARG
+    # activation-quantized GEMV: 1 <= M <= 16, K a multiple of the weight block
+    assert g.lq_gemv_q8act(9, A16, A16, A16, A16, A16, 2, 64, 64, None, 0, None) == FMT
+    assert g.lq_gemv_q8act(0, A16, A16, A16, A16, A16, 0, 64, 64, None, 0, None) == SHAPE
+    assert g.lq_gemv_q8act(0, A16, A16, A16, A16, A16, 17, 64, 64, None, 0, None) == SHAPE
+    assert g.lq_gemv_q8act(2, A16, A16, A16, A16, A16, 2, 64, 96, None, 0, None) == SHAPE   # int8 block 64
+    assert g.lq_gemv_q8act(0, A16 + 8, A16, A16, A16, A16, 2, 64, 64, None, 0, None) == ALIGN
+    assert g.lq_gemv_q8act(0, A16, A16 + 8, A16, A16, A16, 2, 64, 64, None, 0, None) == ALIGN
+    assert g.lq_gemv_q8act(0, A16, A16, A16 + 1, A16, A16, 2, 64, 64, None, 0, None) == ALIGN
+    assert g.lq_gemv_q8act(0, A16, A16, A16, None, A16, 2, 64, 64, None, 0, None) == ARG
+    assert g.lq_gemv_q8act(0, A16, A16, A16, A16, A16 + 2, 2, 64, 64, None, 0, None) == ALIGN
+    assert g.lq_gemv_q8act(0, A16, A16, A16, A16, A16, 2, 64, 64, A16, 64, None) == WS
     # load-time quantization
     assert g.lq_quantize(9, A16, 0, A16, 4, 64, None) == FMT
     assert g.lq_quantize(0, A16, 3, A16, 4, 64, None) == DTYPE
