@@ -230,7 +230,8 @@ struct Q8ActArgs {
 };
 hipError_t launch_quantize_act(int xdt, const void* X, int64_t M, int64_t K, int8_t* q, float* s, int32_t* sum,
                                hipStream_t stream);
-hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, hipStream_t stream);
+// waves: 4 or 16 per workgroup (the units of one K slice are split among them).
+hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, int waves, hipStream_t stream);
 
 // ------------------------------------------------------- conversions ----
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,

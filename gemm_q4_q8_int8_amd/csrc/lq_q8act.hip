@@ -84,12 +84,13 @@ __device__ __forceinline__ int block_dot(const uint32_t (&c)[8], ci32_p x, int I
     return I;
 }
 
-// 4 waves per workgroup split a tile's K slice; UNR units per load batch; MT
-// tokens (one instance per token count, so that the token loop is straight
-// code whose activation loads the compiler can issue ahead).
-template <int FMT, int MT, int UNR>
-__global__ __launch_bounds__(256) void gemv_q8act_kernel(const Q8ActArgs a) {
-    constexpr int W = 4;
+// W waves per workgroup (4, or 16 when K is split several ways: four of the
+// slices then meet in LDS instead of through the workspace) split a tile's K
+// slice; UNR units per load batch; MT tokens (one instance per token count,
+// so that the token loop is straight code whose activation loads the
+// compiler can issue ahead).
+template <int FMT, int MT, int UNR, int W>
+__global__ __launch_bounds__(64 * W) void gemv_q8act_kernel(const Q8ActArgs a) {
     constexpr int P = unit_parts(FMT);
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
@@ -183,7 +184,16 @@ __global__ __launch_bounds__(256) void gemv_q8act_kernel(const Q8ActArgs a) {
     if (w != 0) return;
     float v[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) v[t] = (red[t][0][r] + red[t][1][r]) + (red[t][2][r] + red[t][3][r]);
+    for (int t = 0; t < MT; ++t) {
+        float p[W];
+#pragma unroll
+        for (int j = 0; j < W; ++j) p[j] = red[t][j][r];
+#pragma unroll
+        for (int h = 1; h < W; h *= 2)
+#pragma unroll
+            for (int j = 0; j < W; j += 2 * h) p[j] += p[j + h];
+        v[t] = p[0];
+    }
     const size_t row = size_t(tile) * kTileRows + size_t(r);
     if (S == 1) {
         if (r < nr) {
@@ -210,19 +220,20 @@ __global__ __launch_bounds__(256) void gemv_q8act_kernel(const Q8ActArgs a) {
 }
 
 template <int FMT, int MT>
-hipError_t launch_fmt_mt(const Q8ActArgs& a, hipStream_t stream) {
+hipError_t launch_fmt_mt(const Q8ActArgs& a, int waves, hipStream_t stream) {
     constexpr int UNR = FMT == kQ4_0 ? 4 : (FMT == kI8B64 ? 1 : 2);
-    hipLaunchKernelGGL((gemv_q8act_kernel<FMT, MT, UNR>), dim3(unsigned(int64_t(a.tiles) * a.S)), dim3(256u), 0,
-                       stream, a);
+    const dim3 grid(unsigned(int64_t(a.tiles) * a.S));
+    if (waves == 16) hipLaunchKernelGGL((gemv_q8act_kernel<FMT, MT, UNR, 16>), grid, dim3(1024u), 0, stream, a);
+    else hipLaunchKernelGGL((gemv_q8act_kernel<FMT, MT, UNR, 4>), grid, dim3(256u), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int FMT, int... Ms>
-hipError_t launch_fmt(const Q8ActArgs& a, hipStream_t stream, std::integer_sequence<int, Ms...>) {
-    using Fn = hipError_t (*)(const Q8ActArgs&, hipStream_t);
+hipError_t launch_fmt(const Q8ActArgs& a, int waves, hipStream_t stream, std::integer_sequence<int, Ms...>) {
+    using Fn = hipError_t (*)(const Q8ActArgs&, int, hipStream_t);
     static constexpr Fn table[] = {&launch_fmt_mt<FMT, Ms + 1>...};
     if (a.M < 1 || a.M > int(sizeof...(Ms))) return hipErrorInvalidValue;
-    return table[a.M - 1](a, stream);
+    return table[a.M - 1](a, waves, stream);
 }
 
 }  // namespace
@@ -237,13 +248,14 @@ hipError_t launch_quantize_act(int xdt, const void* X, int64_t M, int64_t K, int
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, hipStream_t stream) {
+hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, int waves, hipStream_t stream) {
+    if (waves != 4 && waves != 16) return hipErrorInvalidValue;
     const auto ms = std::make_integer_sequence<int, kQ8ActMaxTokens>{};
     switch (fmt) {
-        case kQ4_0: return launch_fmt<kQ4_0>(a, stream, ms);
-        case kQ8_0: return launch_fmt<kQ8_0>(a, stream, ms);
-        case kI8B64: return launch_fmt<kI8B64>(a, stream, ms);
-        case kI8B32: return launch_fmt<kI8B32>(a, stream, ms);
+        case kQ4_0: return launch_fmt<kQ4_0>(a, waves, stream, ms);
+        case kQ8_0: return launch_fmt<kQ8_0>(a, waves, stream, ms);
+        case kI8B64: return launch_fmt<kI8B64>(a, waves, stream, ms);
+        case kI8B32: return launch_fmt<kI8B32>(a, waves, stream, ms);
         default: return hipErrorInvalidValue;
     }
 }
