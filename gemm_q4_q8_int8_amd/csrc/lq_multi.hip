@@ -29,7 +29,8 @@
 //     4r..4r+3: one 8- or 16-byte load per unit.
 //   * The k order inside a block is free as long as A and B agree.  Q4_0:
 //     lane group j takes elements 4j..4j+3 and 16+4j..16+4j+3, exactly the
-//     low and high nibbles of code dword j.  int8: lane group j takes
+//     low and high nibbles of code dword j; those activations are staged in
+//     LDS per batch of units (XStage below).  int8: lane group j takes
 //     elements 8j..8j+7 (the two 16-byte parts of a 32-element step are
 //     transposed as double dwords), so its activations are one 16-byte
 //     load.
@@ -74,11 +75,36 @@ __device__ __forceinline__ float scale_of(const MUnit<FMT>& b, int m) {
 struct WaveLoop {
     const uint8_t* cbase;   // code plane of the tile
     const uint8_t* sbase;   // scale plane of the tile
-    const _Float16* xrow;   // activations of this lane's token at its k-set
+    const _Float16* xrow;   // activations of this lane's token at its k-set (int8 formats)
+    const uint8_t* xg;      // activations, M x K fp16 row-major (Q4_0)
+    uint8_t* xs;            // this wave's staging area in LDS (Q4_0)
+    uint32_t x_row;         // byte offset of this lane's token row in it (Q4_0)
+    int M, K;
     uint32_t c_lane, c_unit, c_part, s_unit;
     uint32_t s_row[4];      // scale offsets of rows 4r .. 4r+3 (clamped)
     int ua, ub;             // units [ua, ub)
 };
+
+// Q4_0 activations go through LDS.  Read straight from memory, the A
+// fragments of one unit take two load instructions that each touch 16 token
+// rows (16 cache lines for 512 bytes).  Instead each wave copies the M token
+// rows of its batch's K range (UNR units) into its own LDS area with
+// global_load_lds (1 KB per instruction, a few lines each), then reads the
+// fragments from there.  Row pitch: UNR * 4 + 1 chunks of 16 bytes (odd, so
+// the 16 token rows of a fragment read fall in distinct banks).  Measured on
+// the 151936 x 896 LM head: M = 8 / 16 from 23.2 / 29.5 to 20.5 / 22.5 us,
+// M = 5 unchanged.  The int8 formats read one 16-byte fragment per unit, and
+// staging them was 0.3-1 us slower on every shape measured.
+template <int FMT, int UNR>
+struct XStage {
+    static constexpr int E = unit_elems(FMT);
+    static constexpr int CPU = E / 8;                    // 16-byte chunks per unit and token
+    static constexpr int P16 = UNR * CPU + 1;            // row pitch in chunks
+    static constexpr int kChunks = (16 * P16 + 63) / 64 * 64;
+    static constexpr int kBytes = kChunks * 16;          // per wave
+};
+template <int FMT>
+constexpr bool staged_x() { return FMT == kQ4_0; }
 
 // acc[m][i] += sum over the wave's units of w[4r+m, k] X[4j+i, k].  FULL: the
 // tile has 64 rows, so the four scales of rows 4r..4r+3 are one load.  The
@@ -89,7 +115,27 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
     constexpr int SB = scale_bytes(FMT);
     constexpr int E = unit_elems(FMT);
     constexpr int KS = steps_of<FMT>();
+    using XS = XStage<FMT, UNR>;
     for (int u = L.ua; u < L.ub; u += UNR) {
+        if constexpr (staged_x<FMT>()) {
+            // The batch's activations: lane l of copy i fills chunk
+            // q = 64 i + l of the area: token row t = q / P16 (token
+            // min(t, M - 1)), chunk kc of that row: unit min(u + kc / CPU,
+            // ub - 1), its chunk kc % CPU.  The pad chunk and rows past M
+            // re-read data nobody uses.
+            const int ni = (L.M * XS::P16 + 63) / 64;
+            for (int i = 0; i < ni; ++i) {
+                const int q = 64 * i + (int(threadIdx.x) & 63);
+                const int t = min(q / XS::P16, L.M - 1);
+                const int kc = min(q % XS::P16, UNR * XS::CPU - 1);
+                const int uk = min(u + kc / XS::CPU, L.ub - 1);
+                const size_t off = size_t(t) * size_t(L.K) + size_t(uk) * E + size_t(kc % XS::CPU) * 8;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(L.xg + 2 * off),
+                                                 (__attribute__((address_space(3))) void*)(L.xs + 1024 * i), 16,
+                                                 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         MUnit<FMT> b[UNR];
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
@@ -118,13 +164,10 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
                     else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + L.s_row[m]);
                 }
             }
-            const _Float16* xp = L.xrow + size_t(uu) * E;
+            if constexpr (!staged_x<FMT>()) {
+                const _Float16* xp = L.xrow + size_t(uu) * E;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if constexpr (FMT == kQ4_0) {
-                    b[k].xl[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks);
-                    b[k].xh[ks] = *reinterpret_cast<const u32x2*>(xp + 32 * ks + 16);
-                } else {
+                for (int ks = 0; ks < KS; ++ks) {
                     const u32x4 v = *reinterpret_cast<const u32x4*>(xp + 32 * ks);
                     b[k].xl[ks] = u32x2{v.x, v.y};
                     b[k].xh[ks] = u32x2{v.z, v.w};
@@ -133,6 +176,23 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
         }
         // Every load of the batch is issued before any of its data is used.
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (staged_x<FMT>()) {
+            // The copies into LDS have landed once at most the batch's code
+            // and scale loads (issued after them) are outstanding; then lane
+            // (r, g) reads elements 4g .. 4g+3 and 16+4g .. of each unit from
+            // its token's row.
+            constexpr int kBatchLoads = UNR * (P + (FULL ? 1 : 4));
+            static_assert(kBatchLoads <= 63, "vmcnt range");
+            __builtin_amdgcn_s_waitcnt((kBatchLoads & 15) | (0x7 << 4) | (0xF << 8) | ((kBatchLoads >> 4) << 14));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const uint8_t* xp = L.xs + L.x_row + k * 64 + 8 * (int(threadIdx.x) >> 4 & 3);
+                b[k].xl[0] = *reinterpret_cast<const u32x2*>(xp);
+                b[k].xh[0] = *reinterpret_cast<const u32x2*>(xp + 32);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
             if (u + k >= L.ub) continue;
@@ -175,8 +235,13 @@ template <int FMT, int UNR>
 __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArgs a) {
     constexpr int UB = unit_bytes(FMT);
     constexpr int SB = scale_bytes(FMT);
-    __shared__ float red[4][16][64];
+    // One LDS area: the four waves' activation staging during the loop
+    // (Q4_0), the cross-wave sums after it.
+    constexpr int kStageBytes = staged_x<FMT>() ? 4 * XStage<FMT, UNR>::kBytes : 0;
+    constexpr int kRedBytes = 4 * 16 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
     __shared__ uint32_t last;
+    auto red = reinterpret_cast<float (*)[16][64]>(smem);
 
     // Matrix of this workgroup: the last descriptor whose first workgroup is
     // not after ours (uniform, scalar compares).
@@ -213,7 +278,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     for (int m = 0; m < 4; ++m) L.s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
     // Q4_0 lane group g takes elements 4g..4g+3 and 16+4g.. of a block (the
     // nibbles of code dword g); int8 lane group g takes elements 8g..8g+7.
-    L.xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + (FMT == kQ4_0 ? 4 : 8) * g;
+    L.xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + 8 * g;
+    L.xg = reinterpret_cast<const uint8_t*>(D.x);
+    L.xs = smem + w * XStage<FMT, UNR>::kBytes;
+    L.x_row = uint32_t(min(r, M - 1)) * uint32_t(XStage<FMT, UNR>::P16) * 16u;
+    L.M = M;
+    L.K = D.K;
     L.ua = ua;
     L.ub = ub;
 
@@ -221,8 +291,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     if (full) accumulate<FMT, UNR, true>(L, acc);
     else accumulate<FMT, UNR, false>(L, acc);
 
-    // Sum the four waves' K quarters; wave w then owns token 4g + w of rows
-    // 4r .. 4r+3.
+    // Sum the four waves' K quarters (the staging areas are free once every
+    // wave is past its loop); wave w then owns token 4g + w of rows 4r .. 4r+3.
+    __syncthreads();
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
