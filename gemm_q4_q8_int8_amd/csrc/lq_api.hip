@@ -621,15 +621,18 @@ lq_status lq_gemv_q8act(int32_t fmt, const void* W, const int8_t* q, const float
     LQ_TRY(check_gemv_ws(ws, ws_bytes));
     int cus = 0;
     LQ_TRY(device_cus(&cus));
-    // The K split of the single-token GEMV, with M tokens of partials per
-    // row; a split of LQ_GEMV_WIDE_FROM or more ways moves four slices into
-    // one 16-wave workgroup, as the GEMV does.
+    // q8act_mfma_from(fmt) tokens or more run on the integer matrix cores
+    // with the multi-token GEMV's K split; fewer on the vector dot-product
+    // kernel with the single-token GEMV's (a split of LQ_GEMV_WIDE_FROM or
+    // more ways moves four slices into one 16-wave workgroup, as the GEMV
+    // does).  M tokens of partials per row either way.
+    const bool mfma = M >= lq::q8act_mfma_from(fmt);
     const int64_t tiles = (N + lq::kTileRows - 1) / lq::kTileRows;
     const int64_t nu = K / lq::unit_elems(fmt);
     std::vector<int64_t> S(1, 1);
-    split_k(lq::gemv_min_units(fmt), cus, {tiles}, {nu}, {M}, S);
+    split_k(mfma ? lq::multi_min_units(fmt) : lq::gemv_min_units(fmt), cus, {tiles}, {nu}, {M}, S);
     int waves = 4;
-    if (S[0] >= LQ_GEMV_WIDE_FROM) {
+    if (!mfma && S[0] >= LQ_GEMV_WIDE_FROM) {
         waves = 16;
         S[0] = (S[0] + 3) / 4;
     }
@@ -651,7 +654,8 @@ lq_status lq_gemv_q8act(int32_t fmt, const void* W, const int8_t* q, const float
     a.tiles = int32_t(tiles);
     a.S = int32_t(S[0]);
     a.M = int32_t(M);
-    const hipError_t e = lq::launch_gemv_q8act(fmt, a, waves, static_cast<hipStream_t>(stream));
+    const hipError_t e = mfma ? lq::launch_gemv_q8act_mfma(fmt, a, static_cast<hipStream_t>(stream))
+                              : lq::launch_gemv_q8act(fmt, a, waves, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LQ_OK : hip_fail(e, "activation-quantized GEMV launch");
 }
 

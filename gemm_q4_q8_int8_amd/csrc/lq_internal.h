@@ -210,6 +210,22 @@ hipError_t launch_gemv_multi(int fmt, const MultiArgs& a, hipStream_t stream);
 // scales s and code sums (M x K / 32 each); Y = sum over blocks of
 // (w_scale * s) * (integer block dot product).
 constexpr int kQ8ActMaxTokens = 16;
+// Token counts from which the integer-dot GEMV runs on the matrix cores
+// (fewer run on the vector dot-product kernel).  Measured kernel times, LM
+// head 151936x896 Q4_0 at M = 6 / 8 / 16: 20.7 / 23.7 / 40 us (vector) and
+// 20.7 / 21.5 / 24.7 us (matrix cores); the int8 formats' vector kernel is
+// faster up to M = 8 on every shape measured (Q8_0 8192x2048 at M = 8:
+// 8.1 vs 11.0 us) and the matrix cores at M = 16 are even or ahead (Q8_0
+// 2048x8192: 22.1 vs 16.6 us).
+#ifndef LQ_Q8ACT_MFMA_FROM_Q4
+#define LQ_Q8ACT_MFMA_FROM_Q4 7
+#endif
+#ifndef LQ_Q8ACT_MFMA_FROM_I8
+#define LQ_Q8ACT_MFMA_FROM_I8 16
+#endif
+__host__ __device__ constexpr int q8act_mfma_from(int fmt) {
+    return fmt == kQ4_0 ? LQ_Q8ACT_MFMA_FROM_Q4 : LQ_Q8ACT_MFMA_FROM_I8;
+}
 
 struct Q8ActArgs {
     const uint8_t* codes;   // code plane (tiled)
@@ -232,6 +248,9 @@ hipError_t launch_quantize_act(int xdt, const void* X, int64_t M, int64_t K, int
                                hipStream_t stream);
 // waves: 4 or 16 per workgroup (the units of one K slice are split among them).
 hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, int waves, hipStream_t stream);
+// The same product on the integer matrix cores (4 waves per workgroup, one
+// 64-row tile per K slice; partials of M tokens per slice as above).
+hipError_t launch_gemv_q8act_mfma(int fmt, const Q8ActArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------- conversions ----
 hipError_t launch_repack_gguf(int fmt, const void* src, void* dst, int64_t N, int64_t K,

@@ -18,7 +18,11 @@
 //     high nibbles 16 + 4i .. 16 + 4i + 3, so both dot the activations in
 //     their natural order.  The exact block sum I becomes fp32 (|I| < 2^24)
 //     and is scaled once: acc += fl(ws * s) * I.  Tokens share every code
-//     load; each adds its own dot products.
+//     load; each adds its own dot products, so the vector work grows with
+//     the token count.
+//   * gemv_q8act_mfma_kernel (more tokens, q8act_mfma_from): the same exact
+//     block sums on the integer matrix cores, below.
+#include "lq_frag.h"
 #include "lq_splitk.h"
 
 #include <utility>
@@ -236,6 +240,287 @@ hipError_t launch_fmt(const Q8ActArgs& a, int waves, hipStream_t stream, std::in
     return table[a.M - 1](a, waves, stream);
 }
 
+
+// ------------------------------------------------ matrix-core variant ----
+// The same product for several tokens on the integer matrix cores: one
+// v_mfma_i32_16x16x32_i8 per (16 weight rows, one 32-element block), A = the
+// 16-token activation code fragment, B = the weight codes as int8 (Q4_0: the
+// stored nibbles q + 8, with the accumulator started at -8 x the block's code
+// sum), so the block sums are the same exact integers as above.  Layout as
+// the fp16 multi-token GEMV's: lane (r, g) (r = lane % 16, g = lane / 16)
+// loads tile row 4r + g; four cross-row swaps give lane (r, j) code dword j
+// of rows 4r .. 4r+3; the output lane (r, j) holds tokens 4j .. 4j+3 of
+// rows 4r .. 4r+3.  k order inside a block: Q4_0 lane group j takes elements
+// 4j .. 4j+3 and 16+4j .. 16+4j+3 (the low and high nibbles of code dword
+// j), the int8 formats elements 8j .. 8j+7.
+//
+// Each wave stages its batch's activation codes (token rows of the batch's
+// K range), scales and code sums (block-major, 16 tokens per block) in its
+// own LDS area with global_load_lds; reading them straight from memory
+// would make every load touch 16 token rows.
+template <int FMT, int UNR>
+struct Q8Stage {
+    static constexpr int E = unit_elems(FMT);
+    static constexpr int XB = E / 32;                    // activation blocks per unit
+    static constexpr int CPU = E / 16;                   // 16-byte chunks of codes per unit and token
+    static constexpr int P16 = UNR * CPU + 1;            // code row pitch in chunks (odd: no bank conflicts)
+    static constexpr int kQBytes = (16 * P16 + 63) / 64 * 1024;
+    static constexpr int kSDwords = (UNR * XB * 16 + 63) / 64 * 64;
+    static constexpr int kSums = FMT == kQ4_0 ? 1 : 0;   // code sums staged (Q4_0 only)
+    static constexpr int kBytes = kQBytes + (1 + kSums) * kSDwords * 4;
+};
+
+template <int FMT>
+struct Q8Unit {
+    u32x4 c[unit_parts(FMT)];   // codes of tile row 4r + g
+    uint32_t s[4];              // raw scales of rows 4r .. 4r+3 (as the multi-token GEMV loads them)
+};
+
+template <int FMT, bool FULL>
+__device__ __forceinline__ float q8_scale(const Q8Unit<FMT>& b, int m) {
+    if constexpr (scale_bytes(FMT) == 4) {
+        return __uint_as_float(b.s[m]);
+    } else {
+        const uint32_t v = FULL ? b.s[m >> 1] : b.s[m];
+        const uint16_t h = uint16_t(FULL && (m & 1) ? v >> 16 : v);
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Q8Wave {
+    const uint8_t* cbase;   // code plane of the tile
+    const uint8_t* sbase;   // scale plane of the tile
+    uint8_t* xs;            // this wave's staging area
+    uint32_t c_lane, c_unit, c_part, s_unit;
+    uint32_t s_row[4];
+    uint32_t q_row;         // byte offset of this lane's token row in the staged codes
+    int ua, ub, nb, K;
+};
+
+template <int FMT, int UNR, bool FULL>
+__device__ __forceinline__ void q8_accumulate(const Q8ActArgs& a, const Q8Wave& L, f32x4 (&acc)[4]) {
+    using QS = Q8Stage<FMT, UNR>;
+    constexpr int P = unit_parts(FMT);
+    constexpr int SB = scale_bytes(FMT);
+    constexpr int E = QS::E;
+    constexpr int XB = QS::XB;
+    const int lane = int(threadIdx.x) & 63;
+    const int g = lane >> 4;
+    const int M = a.M;
+    uint8_t* const xq = L.xs;
+    uint8_t* const xsc = L.xs + QS::kQBytes;
+    uint8_t* const xsm = xsc + QS::kSDwords * 4;
+    for (int u = L.ua; u < L.ub; u += UNR) {
+        // Codes: lane l of copy i fills chunk q = 64 i + l: token row
+        // t = q / P16 (token min(t, M - 1)), chunk kc of the row: unit
+        // min(u + kc / CPU, ub - 1), its chunk kc % CPU.  Scales and sums:
+        // dword p = 64 i + l is block slot p / 16 (unit (p / 16) / XB,
+        // sub-block (p / 16) % XB) of token p % 16.  Pads, slack and rows
+        // past M re-read valid data nobody uses.
+        const int ni = (M * QS::P16 + 63) / 64;
+        for (int i = 0; i < ni; ++i) {
+            const int q = 64 * i + lane;
+            const int t = min(q / QS::P16, M - 1);
+            const int kc = min(q % QS::P16, UNR * QS::CPU - 1);
+            const int uk = min(u + kc / QS::CPU, L.ub - 1);
+            const size_t off = size_t(t) * size_t(L.K) + size_t(uk) * E + size_t(kc % QS::CPU) * 16;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.q + off),
+                                             (__attribute__((address_space(3))) void*)(xq + 1024 * i), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < QS::kSDwords / 64; ++i) {
+            const int p = 64 * i + lane;
+            const int bs = p >> 4;
+            const int t = min(p & 15, M - 1);
+            const int uk = min(u + bs / XB, L.ub - 1);
+            const size_t idx = size_t(t) * size_t(L.nb) + size_t(uk) * XB + size_t(bs % XB);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.s + idx),
+                                             (__attribute__((address_space(3))) void*)(xsc + 256 * i), 4, 0, 0);
+            if constexpr (QS::kSums)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a.sum + idx),
+                                                 (__attribute__((address_space(3))) void*)(xsm + 256 * i), 4, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        Q8Unit<FMT> b[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t uu = uint32_t(min(u + k, L.ub - 1));
+            const uint32_t co = uu * L.c_unit + L.c_lane;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                b[k].c[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
+            const uint8_t* sp = L.sbase + uu * L.s_unit;
+            if constexpr (FULL && SB == 2) {
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sp + L.s_row[0]));
+                b[k].s[0] = v.x;
+                b[k].s[1] = v.y;
+            } else if constexpr (FULL) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(sp + L.s_row[0]);
+                b[k].s[0] = v.x;
+                b[k].s[1] = v.y;
+                b[k].s[2] = v.z;
+                b[k].s[3] = v.w;
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if constexpr (SB == 2)
+                        b[k].s[m] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp + L.s_row[m]));
+                    else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + L.s_row[m]);
+                }
+            }
+        }
+        // The copies into LDS were issued before the batch's code and scale
+        // loads, and the vector-memory counter is in order: they have landed
+        // once at most those loads are outstanding.
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int kBatchLoads = UNR * (P + (FULL ? 1 : 4));
+        static_assert(kBatchLoads <= 63, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt((kBatchLoads & 15) | (0x7 << 4) | (0xF << 8) | ((kBatchLoads >> 4) << 14));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            if (u + k >= L.ub) continue;
+            u32x4 t[P];
+            if constexpr (FMT == kQ4_0) {
+                t[0] = frag::xpose(b[k].c[0]);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < XB; ++ks) {
+                    const u32x4 p0 = b[k].c[2 * ks], p1 = b[k].c[2 * ks + 1];
+                    t[2 * ks] = frag::xpose(u32x4{p0.x, p0.z, p1.x, p1.z});
+                    t[2 * ks + 1] = frag::xpose(u32x4{p0.y, p0.w, p1.y, p1.w});
+                }
+            }
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb) {
+                const uint8_t* qp = xq + L.q_row + (k * QS::CPU) * 16 + 32 * xb;
+                uint64_t A;
+                if constexpr (FMT == kQ4_0) {
+                    const uint32_t lo = *reinterpret_cast<const uint32_t*>(qp + 4 * g);
+                    const uint32_t hi = *reinterpret_cast<const uint32_t*>(qp + 16 + 4 * g);
+                    A = uint64_t(lo) | (uint64_t(hi) << 32);
+                } else {
+                    A = *reinterpret_cast<const uint64_t*>(qp + 8 * g);
+                }
+                const int bs = k * XB + xb;
+                const f32x4 sx = *reinterpret_cast<const f32x4*>(xsc + (bs * 16 + 4 * g) * 4);
+                i32x4 c0 = {0, 0, 0, 0};
+                if constexpr (FMT == kQ4_0) c0 = *reinterpret_cast<const i32x4*>(xsm + (bs * 16 + 4 * g) * 4) * -8;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    uint64_t B;
+                    if constexpr (FMT == kQ4_0)
+                        B = uint64_t(t[0][m] & 0x0F0F0F0Fu) | (uint64_t((t[0][m] >> 4) & 0x0F0F0F0Fu) << 32);
+                    else B = uint64_t(t[2 * xb][m]) | (uint64_t(t[2 * xb + 1][m]) << 32);
+                    const i32x4 I = __builtin_amdgcn_mfma_i32_16x16x32_i8(long(A), long(B), c0, 0, 0, 0);
+                    const float ws = q8_scale<FMT, FULL>(b[k], m);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[m][i] = __builtin_fmaf(ws * sx[i], float(I[i]), acc[m][i]);
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int UNR>
+__global__ __launch_bounds__(256) void gemv_q8act_mfma_kernel(const Q8ActArgs a) {
+    constexpr int UB = unit_bytes(FMT);
+    constexpr int SB = scale_bytes(FMT);
+    using QS = Q8Stage<FMT, UNR>;
+    constexpr int kStageBytes = 4 * QS::kBytes;
+    constexpr int kRedBytes = 4 * 16 * 64 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
+    __shared__ uint32_t last;
+    auto red = reinterpret_cast<float (*)[16][64]>(smem);
+
+    const int N = a.N, nu = a.nu, S = a.S, M = a.M;
+    const int local = int(blockIdx.x);
+    const int tile = local / S;
+    const int slice = local - tile * S;
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int lane = int(threadIdx.x) & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nr = min(kTileRows, N - tile * kTileRows);
+    const bool full = nr == kTileRows;
+    const int sa = int(int64_t(nu) * slice / S);
+    const int sb = int(int64_t(nu) * (slice + 1) / S);
+
+    const size_t first = size_t(tile) * kTileRows * size_t(nu);
+    Q8Wave L;
+    L.cbase = a.codes + first * UB;
+    L.sbase = a.scales + first * SB;
+    L.xs = smem + w * QS::kBytes;
+    // Rows past the end of a partial tile are re-read from the last row and
+    // never stored; so are tokens past M.
+    L.c_lane = uint32_t(min(4 * r + g, nr - 1)) * 16u;
+    L.c_unit = uint32_t(nr) * UB;
+    L.c_part = uint32_t(nr) * 16u;
+    L.s_unit = uint32_t(nr) * SB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) L.s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
+    L.q_row = uint32_t(min(r, M - 1)) * uint32_t(QS::P16) * 16u;
+    L.ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / 4);
+    L.ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / 4);
+    L.nb = nu * QS::XB;
+    L.K = nu * QS::E;
+
+    f32x4 acc[4] = {};
+    if (full) q8_accumulate<FMT, UNR, true>(a, L, acc);
+    else q8_accumulate<FMT, UNR, false>(a, L, acc);
+
+    // Sum the four waves' K quarters (the staging areas are free once every
+    // wave is past its loop); wave w then owns token 4g + w of rows 4r .. 4r+3.
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[w][4 * m + i][lane] = acc[m][i];
+    __syncthreads();
+    float v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        v[m] = (red[0][4 * m + w][lane] + red[1][4 * m + w][lane]) +
+               (red[2][4 * m + w][lane] + red[3][4 * m + w][lane]);
+    const int token = 4 * g + w;
+    const size_t row0 = size_t(tile) * kTileRows + size_t(4 * r);
+    if (S == 1) {
+        if (token < M) {
+            float* yp = a.y + size_t(token) * size_t(N) + row0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (4 * r + m < nr) yp[m] = v[m];
+        }
+        return;
+    }
+    // Split K: the hand-off of lq_splitk.h (slice j of token t at rows
+    // (j M + t) pitch of the partials).
+    const size_t pitch = size_t(a.tiles) * kTileRows;
+    const size_t spitch = pitch * size_t(M);
+    if (token < M) {
+        float* pp = a.part + size_t(slice) * spitch + size_t(token) * pitch + row0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) splitk_put(pp + m, v[m]);
+    }
+    splitk_publish();
+    __syncthreads();
+    if (threadIdx.x == 0) last = splitk_arrive(&a.cnt[tile], a.tag, S) ? 1u : 0u;
+    __syncthreads();
+    if (!last) return;
+    if (token < M) {
+        const float* pp = a.part + size_t(token) * pitch + row0;
+        float* yp = a.y + size_t(token) * size_t(N) + row0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float t = sum_slices(pp + m, spitch, S);
+            if (4 * r + m < nr) yp[m] = t;
+        }
+    }
+}
 }  // namespace
 
 hipError_t launch_quantize_act(int xdt, const void* X, int64_t M, int64_t K, int8_t* q, float* s, int32_t* sum,
@@ -248,14 +533,33 @@ hipError_t launch_quantize_act(int xdt, const void* X, int64_t M, int64_t K, int
     return hipGetLastError();
 }
 
+hipError_t launch_gemv_q8act_mfma(int fmt, const Q8ActArgs& a, hipStream_t stream) {
+    const dim3 grid(unsigned(int64_t(a.tiles) * a.S)), block(256u);
+    switch (fmt) {
+        case kQ4_0: hipLaunchKernelGGL((gemv_q8act_mfma_kernel<kQ4_0, 4>), grid, block, 0, stream, a); break;
+        case kQ8_0: hipLaunchKernelGGL((gemv_q8act_mfma_kernel<kQ8_0, 2>), grid, block, 0, stream, a); break;
+        case kI8B64: hipLaunchKernelGGL((gemv_q8act_mfma_kernel<kI8B64, 2>), grid, block, 0, stream, a); break;
+        case kI8B32: hipLaunchKernelGGL((gemv_q8act_mfma_kernel<kI8B32, 2>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Token counts the vector kernel is built for: those below q8act_mfma_from.
+template <int FMT>
+constexpr auto vector_token_counts() {
+    constexpr int n = q8act_mfma_from(FMT) - 1 < kQ8ActMaxTokens ? q8act_mfma_from(FMT) - 1 : kQ8ActMaxTokens;
+    static_assert(n >= 1, "the vector kernel takes at least one token count");
+    return std::make_integer_sequence<int, n>{};
+}
+
 hipError_t launch_gemv_q8act(int fmt, const Q8ActArgs& a, int waves, hipStream_t stream) {
     if (waves != 4 && waves != 16) return hipErrorInvalidValue;
-    const auto ms = std::make_integer_sequence<int, kQ8ActMaxTokens>{};
     switch (fmt) {
-        case kQ4_0: return launch_fmt<kQ4_0>(a, waves, stream, ms);
-        case kQ8_0: return launch_fmt<kQ8_0>(a, waves, stream, ms);
-        case kI8B64: return launch_fmt<kI8B64>(a, waves, stream, ms);
-        case kI8B32: return launch_fmt<kI8B32>(a, waves, stream, ms);
+        case kQ4_0: return launch_fmt<kQ4_0>(a, waves, stream, vector_token_counts<kQ4_0>());
+        case kQ8_0: return launch_fmt<kQ8_0>(a, waves, stream, vector_token_counts<kQ8_0>());
+        case kI8B64: return launch_fmt<kI8B64>(a, waves, stream, vector_token_counts<kI8B64>());
+        case kI8B32: return launch_fmt<kI8B32>(a, waves, stream, vector_token_counts<kI8B32>());
         default: return hipErrorInvalidValue;
     }
 }

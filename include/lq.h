@@ -315,7 +315,8 @@ lq_status lq_quantize_act(const void* X, int32_t xdt, int64_t M, int64_t K,
  * two activation blocks), and q, s, sum as lq_quantize_act writes them (sum
  * is read for LQ_Q4_0 only, but must be valid for every format).  Every
  * weight is read once for all M tokens.  The block sums I are exact (int8
- * dot products with int32 accumulation); each is scaled by fl(ws * s) and
+ * dot products with int32 accumulation: on the vector units for few tokens,
+ * on the integer matrix cores for more); each is scaled by fl(ws * s) and
  * accumulated in fp32.  Accuracy: |Y - Y_q| <= 1e-4 * sum_b |ws s I| + 1e-6
  * per output, Y_q the exact value of the sum above.  W: packed N x K; q / s /
  * sum: M tokens of K codes, K/32 scales and K/32 sums (alignment as in

@@ -9,6 +9,8 @@ variants for drafted tokens ("Speculative decoding").  Bars:
   * product: per output |Y - Y_q| <= 1e-4 * sum_b |ws s I| + 1e-6 against the
     oracle's value of the same quantized product (the integer block sums are
     exact on both sides; only the fp32 scaling and accumulation round);
+  * both kernels (vector dot products for few tokens, integer matrix cores
+    for more) on every format;
   * exact case: unit weight scales and integer activations whose blocks reach
     127 (so s = 1 and q = x) make every term an integer; with K <= 1024 every
     partial sum is an integer below 2^24, so Y must equal the integer product
@@ -135,6 +137,11 @@ Q8ACT_SHAPES = [
     ("i8b64", 16, 130, 8192), ("i8b64", 9, 5, 30720), ("i8b64", 1, 1500, 512),
     ("i8b32", 1, 3, 32), ("i8b32", 2, 70, 512), ("i8b32", 4, 130, 8192), ("i8b32", 15, 1100, 1024),
     ("i8b32", 12, 20000, 256),
+    # the matrix-core kernel (Q4_0 from 7 tokens, the int8 formats at 16):
+    # partial tiles, K split, one-block rows
+    ("q4_0", 7, 1, 32), ("q4_0", 7, 200, 4096), ("q4_0", 11, 64, 25600), ("q4_0", 16, 3000, 640),
+    ("q8_0", 16, 100, 2048), ("q8_0", 16, 3, 32), ("i8b64", 16, 1, 64), ("i8b32", 16, 300, 1024),
+    ("i8b32", 16, 5, 30720),
 ]
 
 
@@ -173,7 +180,8 @@ def unit_scale_weights(fmt, seed, N, K):
 
 @pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 5, 130, 1024), ("q8_0", 16, 70, 1024),
                                        ("i8b64", 3, 200, 1024), ("i8b32", 16, 64, 512),
-                                       ("q4_0", 1, 17, 1024), ("q8_0", 9, 1, 992)])
+                                       ("q4_0", 1, 17, 1024), ("q8_0", 9, 1, 992),
+                                       ("q4_0", 9, 70, 1024), ("i8b64", 16, 130, 1024)])
 def test_q8act_exact_integers(oracle, fmt, M, N, K):
     say("gemv_q8act exact integers", fmt, M, N, K)
     w, s = unit_scale_weights(fmt, 4100 + N, N, K)
