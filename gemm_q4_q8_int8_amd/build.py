@@ -27,10 +27,11 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Werror", "-Wno-unused-command-line-argument"]
 
 
-# Per-source extra flags.  The multi-token GEMV takes its MFMA results in
-# ordinary VGPRs (the compiler otherwise routes them through accumulation
-# registers and copies each one back).
-EXTRA = {"lq_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The multi-token GEMVs (fp16 and integer) take
+# their MFMA results in ordinary VGPRs (the compiler otherwise routes them
+# through accumulation registers and copies each one back).
+EXTRA = {"lq_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "lq_q8act.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
