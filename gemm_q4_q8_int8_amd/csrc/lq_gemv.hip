@@ -253,8 +253,15 @@ __device__ __forceinline__ void unit_fma(const Unit<FMT>& b, const void* xv, siz
 }
 
 // Largest batch of units one wave loads before computing them (register
-// budget: the codes of a batch stay live).
+// budget: the codes of a batch stay live).  Q8_0 / int8 block-32: one-unit
+// loads of 2 KB per wave, 4 per batch for one or two tokens (the Q8_0 layer
+// launch: 13.92 -> 13.73-13.84 us against batches of 2; the layer at two
+// tokens 15.04 -> 14.49 us), 2 for more tokens (four tokens with batches of
+// 4: 16.95 -> 18.11 us).
 constexpr int unroll_cap(int fmt) { return fmt == kQ4_0 ? LQ_GEMV_UNR_Q4 : (fmt == kI8B64 ? LQ_GEMV_UNR_I8 : LQ_GEMV_UNR_Q8); }
+inline int unroll_cap(int fmt, int mt) {
+    return (fmt == kQ8_0 || fmt == kI8B32) && mt > 2 ? LQ_GEMV_UNR_Q8_TOKENS : unroll_cap(fmt);
+}
 
 // W waves per workgroup split a tile's K slice W ways (4, or 16 for
 // launches whose matrices would otherwise split K across 4+ workgroups: the
@@ -545,13 +552,13 @@ hipError_t launch_unr(int unr, const GemvArgs& a, hipStream_t stream) {
 // matrix on its own, e.g. one decoder layer's q/k/v or o) has too few loads
 // in flight with one-unit batches; it takes batches of at least two units.
 constexpr int64_t kFewWaves = 4096;
-int launch_unroll(int fmt, int waves, const GemvArgs& a) {
+int launch_unroll(int fmt, int mt, int waves, const GemvArgs& a) {
     int u = 1;
     for (int i = 0; i < a.count; ++i) {
         const int slice = (a.d[i].nu + a.d[i].S - 1) / a.d[i].S;
         u = max(u, (slice + waves - 1) / waves);
     }
-    int cap = unroll_cap(fmt);
+    int cap = unroll_cap(fmt, mt);
     if (int64_t(a.total_wgs) * waves < kFewWaves) cap = max(cap, 2);
     const int batches = (u + cap - 1) / cap;
     return (u + batches - 1) / batches;
@@ -570,7 +577,7 @@ hipError_t launch_tokens(int waves, int mt, int unr, const GemvArgs& a, hipStrea
 template <int FMT>
 hipError_t launch_fmt(int xdt, int waves, int mt, const GemvArgs& a, hipStream_t stream) {
     constexpr int CAP = unroll_cap(FMT) > 2 ? unroll_cap(FMT) : 2;
-    const int unr = launch_unroll(FMT, waves, a);
+    const int unr = launch_unroll(FMT, mt, waves, a);
     if (mt > 1) {
         if (xdt != kF16 || mt > gemv_max_tokens(FMT)) return hipErrorInvalidValue;
         return launch_tokens<FMT, gemv_max_tokens(FMT)>(waves, mt, unr, a, stream);

@@ -89,7 +89,12 @@ constexpr int64_t kMaxSlices = 4096;
 #define LQ_GEMV_UNR_Q4 8
 #endif
 #ifndef LQ_GEMV_UNR_Q8
-#define LQ_GEMV_UNR_Q8 2
+#define LQ_GEMV_UNR_Q8 4
+#endif
+// The same for Q8_0 and int8 block-32 launches of three or more tokens
+// (their activations take the registers).
+#ifndef LQ_GEMV_UNR_Q8_TOKENS
+#define LQ_GEMV_UNR_Q8_TOKENS 2
 #endif
 #ifndef LQ_GEMV_UNR_I8
 #define LQ_GEMV_UNR_I8 1
