@@ -599,7 +599,7 @@ hipError_t launch_sub_tokens(int xdt, int mt, const GemvArgs& a, hipStream_t str
     if constexpr (MT > 1) {
         if (mt < MT) return launch_sub_tokens<FMT, MT - 1>(xdt, mt, a, stream);
     }
-    constexpr int CAP = MT == 1 ? 4 : 2;
+    constexpr int CAP = MT == 1 ? LQ_GEMV_SUB_UNR : 2;
     int u = 1;
     for (int i = 0; i < a.count; ++i) u = max(u, (a.d[i].nu + 15) / 16);
     const int batches = (u + CAP - 1) / CAP;

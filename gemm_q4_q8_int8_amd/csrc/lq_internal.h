@@ -99,6 +99,11 @@ constexpr int64_t kMaxSlices = 4096;
 #ifndef LQ_GEMV_UNR_I8
 #define LQ_GEMV_UNR_I8 1
 #endif
+// Most units a sub-tile GEMV wave (launch_gemv_sub) loads before computing
+// them, one token.
+#ifndef LQ_GEMV_SUB_UNR
+#define LQ_GEMV_SUB_UNR 4
+#endif
 // Fewest units a wave keeps when K is split, per format (a unit is 1, 2 or
 // 4 KB of codes per wave for Q4_0, Q8_0, int8 block-64).
 #ifndef LQ_GEMV_MIN_UNITS_Q4
