@@ -318,7 +318,8 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
     }
     std::vector<int64_t> Ms(n);
     for (int i = 0; i < n; ++i) Ms[i] = g[i]->M;
-    split_k(lq::multi_min_units(fmt), cus, tiles, nu, Ms, S);
+    const int64_t most_tokens = *std::max_element(Ms.begin(), Ms.end());
+    split_k(lq::multi_min_units(fmt, most_tokens), cus, tiles, nu, Ms, S);
     if (!ws.cnt)
         for (int i = 0; i < n; ++i) S[i] = 1;
     float* part = ws.part;
@@ -630,7 +631,7 @@ lq_status lq_gemv_q8act(int32_t fmt, const void* W, const int8_t* q, const float
     const int64_t tiles = (N + lq::kTileRows - 1) / lq::kTileRows;
     const int64_t nu = K / lq::unit_elems(fmt);
     std::vector<int64_t> S(1, 1);
-    split_k(mfma ? lq::multi_min_units(fmt) : lq::gemv_min_units(fmt), cus, {tiles}, {nu}, {M}, S);
+    split_k(mfma ? lq::multi_min_units(fmt, M) : lq::gemv_min_units(fmt), cus, {tiles}, {nu}, {M}, S);
     int waves = 4;
     if (!mfma && S[0] >= LQ_GEMV_WIDE_FROM) {
         waves = 16;

@@ -126,9 +126,32 @@ constexpr int64_t kMaxSlices = 4096;
 inline int gemv_min_units(int fmt) {
     return fmt == kQ4_0 ? LQ_GEMV_MIN_UNITS_Q4 : (fmt == kI8B64 ? LQ_GEMV_MIN_UNITS_I8 : LQ_GEMV_MIN_UNITS_Q8);
 }
-// The same for the multi-token GEMV, whose split K also moves M tokens of
-// partial sums per row through the workspace.
-inline int multi_min_units(int fmt) { return fmt == kI8B64 ? 2 : 8; }
+// The same for the multi-token GEMV (4-wave workgroups), whose split K also
+// moves M tokens of partial sums per row through the workspace, so it pays
+// to split less: in grouped launches the K = 2048 matrices of a layer are
+// best left unsplit and a long-K matrix split a few ways.  Measured on
+// grouped layers (M = 5 / 8 / 12 / 16): the Q8_0 layer from 21.3 / 22.2 /
+// 24.9 / 28.0 us (8 units) to 17.8 / 17.9 / 18.9 / 19.6 (16; 12 and 24 were
+// slower), the Q4_0 2048 / 11008 FFN from 21.6 / 22.6 / 25.4 / 28.3 (8) to
+// 16.9 / 17.3 / 18.1 / 19.0 (16; 32 and 64 slower), the int8 block-64 layer
+// from 22.5 / 24.3 / 27.8 / 23.0 (2 units of 64 weights) to 17.0 / 17.6 (4,
+// M <= 8) and 18.9 / 20.0 (8, M > 8).
+#ifndef LQ_MULTI_MIN_UNITS_Q4
+#define LQ_MULTI_MIN_UNITS_Q4 16
+#endif
+#ifndef LQ_MULTI_MIN_UNITS
+#define LQ_MULTI_MIN_UNITS 16
+#endif
+#ifndef LQ_MULTI_MIN_UNITS_I8
+#define LQ_MULTI_MIN_UNITS_I8 4
+#endif
+#ifndef LQ_MULTI_MIN_UNITS_I8_MANY
+#define LQ_MULTI_MIN_UNITS_I8_MANY 8
+#endif
+inline int multi_min_units(int fmt, int64_t M) {
+    if (fmt == kI8B64) return M <= 8 ? LQ_MULTI_MIN_UNITS_I8 : LQ_MULTI_MIN_UNITS_I8_MANY;
+    return fmt == kQ4_0 ? LQ_MULTI_MIN_UNITS_Q4 : LQ_MULTI_MIN_UNITS;
+}
 
 struct GemvDesc {
     const uint8_t* codes;   // code plane (tiled)
