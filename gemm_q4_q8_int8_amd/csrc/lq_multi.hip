@@ -213,18 +213,24 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
             half8_t xa[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) xa[ks] = x_frag<FMT>(b[k].xl[ks], b[k].xh[ks]);
+            // All four row groups' block sums first, then their scaling: an
+            // FMA right behind the MFMA it reads would wait for its result.
+            f32x4 sum[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+                sum[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     half8_t wb;
                     if constexpr (FMT == kQ4_0) wb = q4_frag(t[0][m]);
                     else wb = i8_frag(t[2 * ks][m], t[2 * ks + 1][m]);
-                    sum = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ks], wb, sum, 0, 0, 0);
+                    sum[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ks], wb, sum[m], 0, 0, 0);
                 }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
                 const float d = scale_of<FMT, FULL>(b[k], m);
-                acc[m] = __builtin_elementwise_fma(f32x4{d, d, d, d}, sum, acc[m]);
+                acc[m] = __builtin_elementwise_fma(f32x4{d, d, d, d}, sum[m], acc[m]);
             }
         }
     }

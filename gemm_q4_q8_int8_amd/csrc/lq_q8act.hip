@@ -411,16 +411,22 @@ __device__ __forceinline__ void q8_accumulate(const Q8ActArgs& a, const Q8Wave& 
                 const f32x4 sx = *reinterpret_cast<const f32x4*>(xsc + (bs * 16 + 4 * g) * 4);
                 i32x4 c0 = {0, 0, 0, 0};
                 if constexpr (FMT == kQ4_0) c0 = *reinterpret_cast<const i32x4*>(xsm + (bs * 16 + 4 * g) * 4) * -8;
+                // The four row groups' block sums first, then their scaling
+                // (a use right behind the MFMA would wait for its result).
+                i32x4 I[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     uint64_t B;
                     if constexpr (FMT == kQ4_0)
                         B = uint64_t(t[0][m] & 0x0F0F0F0Fu) | (uint64_t((t[0][m] >> 4) & 0x0F0F0F0Fu) << 32);
                     else B = uint64_t(t[2 * xb][m]) | (uint64_t(t[2 * xb + 1][m]) << 32);
-                    const i32x4 I = __builtin_amdgcn_mfma_i32_16x16x32_i8(long(A), long(B), c0, 0, 0, 0);
+                    I[m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(long(A), long(B), c0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
                     const float ws = q8_scale<FMT, FULL>(b[k], m);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[m][i] = __builtin_fmaf(ws * sx[i], float(I[i]), acc[m][i]);
+                    for (int i = 0; i < 4; ++i) acc[m][i] = __builtin_fmaf(ws * sx[i], float(I[m][i]), acc[m][i]);
                 }
             }
         }
