@@ -260,3 +260,64 @@ def test_q8act_lm_head_full_size(oracle, M):
     Yr, S = oracle.gemv_q8act(ORACLE_FMT["q4_0"], ws_, ss_, qr[0], qr[1], M, len(rows), K)
     r = gu.ratio(Y[:, rows], Yr, S, Q8ACT_REL, Q8ACT_ABS)
     assert r <= 1.0, f"tolerance ratio {r}"
+
+
+def test_q8act_graph_replays_and_two_streams(oracle):
+    """Quantization plus both product kernels, with K split across
+    workgroups (few tiles, long rows), captured in one graph and replayed
+    several times with eager runs in between: every replay equals the eager
+    result bit for bit.  Then the same work on two streams at once, each
+    with its own workspace, gives the same bits."""
+    say("gemv_q8act graph replays and two streams")
+    cases = [("q4_0", 3, 96, 11008), ("q4_0", 12, 130, 4096), ("q8_0", 16, 64, 8192), ("i8b64", 2, 200, 5632)]
+    bufs = []
+    for i, (fmt, M, N, K) in enumerate(cases):
+        w, s = make(fmt, 3600 + i, N, K)
+        X = lqgen.activations(3700 + i, M * K, np.float32).reshape(M, K)
+        Xd = to_device(X)
+        q = torch.empty(M * K, dtype=torch.int8, device="cuda")
+        sc = torch.empty(M * K // 32, dtype=torch.float32, device="cuda")
+        t = torch.empty(M * K // 32, dtype=torch.int32, device="cuda")
+        Y = torch.zeros(M * N, device="cuda")
+        bufs.append((fmt, M, N, K, w, s, X, Xd, gu.upload(fmt, w, s, N, K), q, sc, t, Y))
+
+    def run(ws, sel=None):
+        for fmt, M, N, K, _, _, _, Xd, Wd, q, sc, t, Y in (bufs if sel is None else sel):
+            lq.lq_quantize_act(Xd, M, K, q, sc, t)
+            lq.lq_gemv_q8act(gu.FMT[fmt], Wd, q, sc, t, Y, M, N, K, ws=ws)
+
+    run(gu.gemv_ws())
+    torch.cuda.synchronize()
+    eager = [b[-1].clone() for b in bufs]
+    for (fmt, M, N, K, w, s, X, *_), y in zip(bufs, eager):
+        qr, sr, _ = oracle.quantize_act(X, M, K)
+        Yr, S = oracle.gemv_q8act(ORACLE_FMT[fmt], w, s, qr, sr, M, N, K)
+        assert gu.ratio(y.cpu().numpy().reshape(M, N), Yr, S, Q8ACT_REL, Q8ACT_ABS) <= 1.0, fmt
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        run(gu.gemv_ws())
+    for rep in range(3):
+        for b in bufs:
+            b[-1].fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(b[-1], e), f"replay {rep} differs from the eager result ({b[0]}, M={b[1]})"
+        run(gu.gemv_ws())
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert torch.equal(b[-1], e), f"eager run after replay {rep} differs"
+    # two streams at once, each with its own workspace
+    for b in bufs:
+        b[-1].fill_(-1.0)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        run(gu.gemv_ws(1), bufs[0::2])
+    with torch.cuda.stream(s2):
+        run(gu.gemv_ws(2), bufs[1::2])
+    torch.cuda.synchronize()
+    for b, e in zip(bufs, eager):
+        assert torch.equal(b[-1], e), f"two-stream run differs ({b[0]}, M={b[1]})"
