@@ -230,6 +230,7 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
             o.cnt = nullptr;
             wgs += tiles[i] * parts;
         }
+        lq::fill_wg0_table(a.wg0, a.d, n);
         a.count = n;
         a.total_wgs = int32_t(wgs);
         const hipError_t e = lq::launch_gemv_sub(fmt, xdt, mt, a, stream);
@@ -280,6 +281,7 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
         wgs += tiles[i] * S[i];
         if (wgs > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
     }
+    lq::fill_wg0_table(a.wg0, a.d, n);
     a.tag = lq::next_splitk_tag();
     a.count = n;
     a.total_wgs = int32_t(wgs);
@@ -354,6 +356,7 @@ lq_status launch_multi_chunk(int fmt, const std::vector<const lq_gemv_multi_desc
         wgs += tiles[i] * S[i];
         if (wgs > INT32_MAX) return fail(LQ_ERR_SHAPE, "too many rows in one grouped launch");
     }
+    lq::fill_wg0_table(a.wg0, a.d, n);
     a.tag = lq::next_splitk_tag();
     a.count = n;
     a.total_wgs = int32_t(wgs);

@@ -100,6 +100,7 @@ struct GemmMat {
 };
 
 struct GemmArgs {
+    int32_t wg0[kMaxGemmGroup];   // mat[i].wg0, INT32_MAX past count (find_matrix)
     GemmMat mat[kMaxGemmGroup];
     const _Float16* X;        // M x K row-major
     int32_t count;            // matrices
@@ -165,14 +166,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(const GemmArgs a
     // K slice.
     int L = blockIdx.x;
     if (a.remap) L = (L % 8) * int(gridDim.x / 8) + L / 8;
-    int mi = 0;
-    for (int i = 1; i < a.count; ++i) mi += L >= a.mat[i].wg0 ? 1 : 0;
-    const GemmMat& G = a.mat[mi];
+    const GemmMat& G = a.mat[find_matrix(a.wg0, L)];
     const int local = L - G.wg0;
-    const int tm = local % a.tiles_m;
-    const int rest = local / a.tiles_m;
-    const int tn = rest % G.tiles_n;
-    const int ks = rest / G.tiles_n;
+    const int rest = int(uint32_t(local) / uint32_t(a.tiles_m));
+    const int tm = local - rest * a.tiles_m;
+    const int ks = int(uint32_t(rest) / uint32_t(G.tiles_n));
+    const int tn = rest - ks * G.tiles_n;
     const int m0 = tm * BM;
     const int u0 = ks * a.us;
     const int nst = min(a.nu, u0 + a.us) - u0;   // steps (blocks) of this slice
@@ -492,14 +491,12 @@ __global__ __launch_bounds__(256, 1) void gemm_wave_kernel(const GemmArgs a) {
 
     int Lw = blockIdx.x;
     if (a.remap) Lw = (Lw % 8) * int(gridDim.x / 8) + Lw / 8;
-    int mi = 0;
-    for (int i = 1; i < a.count; ++i) mi += Lw >= a.mat[i].wg0 ? 1 : 0;
-    const GemmMat& G = a.mat[mi];
+    const GemmMat& G = a.mat[find_matrix(a.wg0, Lw)];
     const int local = Lw - G.wg0;
-    const int tm = local % a.tiles_m;
-    const int rest = local / a.tiles_m;
-    const int tn = rest % G.tiles_n;
-    const int ks = rest / G.tiles_n;
+    const int rest = int(uint32_t(local) / uint32_t(a.tiles_m));
+    const int tm = local - rest * a.tiles_m;
+    const int ks = int(uint32_t(rest) / uint32_t(G.tiles_n));
+    const int tn = rest - ks * G.tiles_n;
     const int m0 = tm * C::BM;
     const int u0 = ks * a.us;
     const int nst = min(a.nu, u0 + a.us) - u0;
@@ -884,6 +881,7 @@ hipError_t launch_gemm_tile(int fmt, const void* const* W, float* const* Y, cons
         wgs += int64_t(p.tiles_m) * g.tiles_n * p.S;
     }
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    fill_wg0_table(a.wg0, a.mat, count);
     a.X = static_cast<const _Float16*>(X);
     a.count = count;
     a.M = int32_t(M);

@@ -276,12 +276,8 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     constexpr int SB = scale_bytes(FMT);
     __shared__ float red[MT][W][kTileRows];
 
-    // Matrix of this workgroup: the last descriptor whose first workgroup is
-    // not after ours (uniform, scalar compares).
     const int bid = blockIdx.x;
-    int di = 0;
-    for (int i = 1; i < a.count; ++i) di += bid >= a.d[i].wg0 ? 1 : 0;
-    const GemvDesc& D = a.d[di];
+    const GemvDesc& D = a.d[find_matrix(a.wg0, bid)];
     const int N = D.N, nu = D.nu, S = D.S;
     const int local = bid - D.wg0;
     // Units [sa, sb) of this workgroup: slice `slice` of S.  (Unsplit
@@ -289,10 +285,9 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     // noticeable share of the wave's scalar work.)
     int tile = local, slice = 0, sa = 0, sb = nu;
     if (S > 1) {
-        tile = local / S;
+        tile = int(uint32_t(local) / uint32_t(S));
         slice = local - tile * S;
-        sa = int(int64_t(nu) * slice / S);
-        sb = int(int64_t(nu) * (slice + 1) / S);
+        slice_units(nu, S, slice, sa, sb);
     }
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int r = int(threadIdx.x) & 63;
@@ -443,9 +438,7 @@ __global__ __launch_bounds__(1024) void gemv_sub_kernel(const GemvArgs a) {
     __shared__ float red[MT][W][kTileRows];
 
     const int bid = blockIdx.x;
-    int di = 0;
-    for (int i = 1; i < a.count; ++i) di += bid >= a.d[i].wg0 ? 1 : 0;
-    const GemvDesc& D = a.d[di];
+    const GemvDesc& D = a.d[find_matrix(a.wg0, bid)];
     const int N = D.N, nu = D.nu;
     const int local = bid - D.wg0;
     const int tile = local / P;

@@ -249,15 +249,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     __shared__ uint32_t last;
     auto red = reinterpret_cast<float (*)[16][64]>(smem);
 
-    // Matrix of this workgroup: the last descriptor whose first workgroup is
-    // not after ours (uniform, scalar compares).
     const int bid = int(blockIdx.x);
-    int di = 0;
-    for (int i = 1; i < a.count; ++i) di += bid >= a.d[i].wg0 ? 1 : 0;
-    const MultiDesc& D = a.d[di];
+    const MultiDesc& D = a.d[find_matrix(a.wg0, bid)];
     const int N = D.N, nu = D.nu, S = D.S, M = D.M;
     const int local = bid - D.wg0;
-    const int tile = local / S;
+    const int tile = int(uint32_t(local) / uint32_t(S));
     const int slice = local - tile * S;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int lane = int(threadIdx.x) & 63;
@@ -265,8 +261,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     const int nr = min(kTileRows, N - tile * kTileRows);
     const bool full = nr == kTileRows;
 
-    const int sa = int(int64_t(nu) * slice / S);
-    const int sb = int(int64_t(nu) * (slice + 1) / S);
+    int sa, sb;
+    slice_units(nu, S, slice, sa, sb);
     const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / 4);
     const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / 4);
 

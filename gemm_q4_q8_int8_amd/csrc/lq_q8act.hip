@@ -106,10 +106,9 @@ __global__ __launch_bounds__(64 * W) void gemv_q8act_kernel(const Q8ActArgs a) {
     const int local = blockIdx.x;
     int tile = local, slice = 0, sa = 0, sb = nu;
     if (S > 1) {
-        tile = local / S;
+        tile = int(uint32_t(local) / uint32_t(S));
         slice = local - tile * S;
-        sa = int(int64_t(nu) * slice / S);
-        sb = int(int64_t(nu) * (slice + 1) / S);
+        slice_units(nu, S, slice, sa, sb);
     }
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int r = int(threadIdx.x) & 63;
@@ -446,15 +445,15 @@ __global__ __launch_bounds__(256) void gemv_q8act_mfma_kernel(const Q8ActArgs a)
 
     const int N = a.N, nu = a.nu, S = a.S, M = a.M;
     const int local = int(blockIdx.x);
-    const int tile = local / S;
+    const int tile = int(uint32_t(local) / uint32_t(S));
     const int slice = local - tile * S;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     const int lane = int(threadIdx.x) & 63;
     const int r = lane & 15, g = lane >> 4;
     const int nr = min(kTileRows, N - tile * kTileRows);
     const bool full = nr == kTileRows;
-    const int sa = int(int64_t(nu) * slice / S);
-    const int sb = int(int64_t(nu) * (slice + 1) / S);
+    int sa, sb;
+    slice_units(nu, S, slice, sa, sb);
 
     const size_t first = size_t(tile) * kTileRows * size_t(nu);
     Q8Wave L;
