@@ -315,23 +315,35 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
     for (int u = ua; u < ub; u += UNR) {
+        // fp16 scales stream past the caches like the codes: as cached
+        // 2-byte loads they cost the Q8_0 decoder layer 7 % of its time.
+        // (The fp32 scales of int8 block-64 measured 1 % faster cached.)
         Unit<FMT> b[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const uint32_t uu = uint32_t(min(u + k, ub - 1));
-            const uint32_t co = uu * c_unit + c_lane;
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                b[k].c[p] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(cbase + co + uint32_t(p) * c_part));
-            // fp16 scales stream past the caches like the codes: as cached
-            // 2-byte loads they cost the Q8_0 decoder layer 7 % of its time.
-            // (The fp32 scales of int8 block-64 measured 1 % faster cached.)
-            const uint32_t so = uu * s_unit + s_lane;
+        auto load_scale = [&](int k) {
+            const uint32_t so = uint32_t(min(u + k, ub - 1)) * s_unit + s_lane;
             if constexpr (SB == 2)
                 b[k].s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + so));
             else
                 b[k].s = *reinterpret_cast<const uint32_t*>(sbase + so);
+        };
+        auto load_codes = [&](int k) {
+            const uint32_t co = uint32_t(min(u + k, ub - 1)) * c_unit + c_lane;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                b[k].c[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(cbase + co + uint32_t(p) * c_part));
+        };
+        if constexpr (scales_first(FMT)) {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_scale(k);
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_codes(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                load_codes(k);
+                load_scale(k);
+            }
         }
         // Every load of the batch is issued before any of its data is used,
         // and every slot is computed: a branch per slot let the compiler sink
@@ -474,14 +486,17 @@ __global__ __launch_bounds__(1024) void gemv_sub_kernel(const GemvArgs a) {
         uint32_t sc[UNR];
         XT x[UNR][MT][XV];
 #pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const uint32_t uu = uint32_t(min(u + k, ub - 1));
-            c[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + uu * c_unit + c_lane));
-            const uint32_t so = uu * s_unit + s_lane;
+        for (int k = 0; k < UNR; ++k) {   // scales first (scales_first: P > 1 here)
+            const uint32_t so = uint32_t(min(u + k, ub - 1)) * s_unit + s_lane;
             if constexpr (SB == 2)
                 sc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + so));
             else
                 sc[k] = *reinterpret_cast<const uint32_t*>(sbase + so);
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t uu = uint32_t(min(u + k, ub - 1));
+            c[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + uu * c_unit + c_lane));
 #pragma unroll
             for (int t = 0; t < MT; ++t)
 #pragma unroll

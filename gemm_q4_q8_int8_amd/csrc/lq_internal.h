@@ -26,6 +26,13 @@ constexpr int kTileRows = 64;
 __host__ __device__ constexpr int unit_elems(int fmt) { return fmt == kI8B64 ? 64 : 32; }
 __host__ __device__ constexpr int unit_parts(int fmt) { return fmt == kQ4_0 ? 1 : (fmt == kI8B64 ? 4 : 2); }
 __host__ __device__ constexpr int unit_bytes(int fmt) { return 16 * unit_parts(fmt); }
+// Order of the loads of one GEMV batch: all the units' scale loads before
+// their code loads for formats whose unit has several 16-byte code parts
+// (Q8_0 decoder layer 13.0 -> 12.9 us, the layer at 2 / 4 / 16 tokens 3 %
+// faster); for Q4_0 each unit's scale load right after its code load (the
+// LM head took 14.8 us with the scales first and 15.4 us with all codes,
+// then all scales, against 14.4 us).
+__host__ __device__ constexpr bool scales_first(int fmt) { return unit_parts(fmt) > 1; }
 // fp32 scales (int8 block-64 and block-32): the codes stay exact and the
 // scale multiplies fp32 sums; fp16 scales (Q4_0, Q8_0).
 __host__ __device__ constexpr bool fp32_scale(int fmt) { return fmt == kI8B64 || fmt == kI8B32; }

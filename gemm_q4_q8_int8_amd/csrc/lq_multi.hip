@@ -137,14 +137,8 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
             __builtin_amdgcn_sched_barrier(0);
         }
         MUnit<FMT> b[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
+        auto load_scale = [&](int k) {
             const uint32_t uu = uint32_t(min(u + k, L.ub - 1));
-            const uint32_t co = uu * L.c_unit + L.c_lane;
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                b[k].c[p] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
             const uint8_t* sp = L.sbase + uu * L.s_unit;
             if constexpr (FULL && SB == 2) {
                 const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sp + L.s_row[0]));
@@ -164,6 +158,14 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
                     else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + L.s_row[m]);
                 }
             }
+        };
+        auto load_codes = [&](int k) {
+            const uint32_t uu = uint32_t(min(u + k, L.ub - 1));
+            const uint32_t co = uu * L.c_unit + L.c_lane;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                b[k].c[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
             if constexpr (!staged_x<FMT>()) {
                 const _Float16* xp = L.xrow + size_t(uu) * E;
 #pragma unroll
@@ -172,6 +174,18 @@ __device__ __forceinline__ void accumulate(const WaveLoop& L, f32x4 (&acc)[4]) {
                     b[k].xl[ks] = u32x2{v.x, v.y};
                     b[k].xh[ks] = u32x2{v.z, v.w};
                 }
+            }
+        };
+        if constexpr (scales_first(FMT)) {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_scale(k);
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_codes(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                load_codes(k);
+                load_scale(k);
             }
         }
         // Every load of the batch is issued before any of its data is used.

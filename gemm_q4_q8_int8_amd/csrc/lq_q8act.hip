@@ -132,16 +132,28 @@ __global__ __launch_bounds__(64 * W) void gemv_q8act_kernel(const Q8ActArgs a) {
     for (int u = ua; u < ub; u += UNR) {
         u32x4 cw[UNR][P];
         uint32_t sw[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const uint32_t uu = uint32_t(min(u + k, ub - 1));
-            const uint32_t co = uu * c_unit + c_lane;
+        auto load_scale = [&](int k) {
+            const uint32_t so = uint32_t(min(u + k, ub - 1)) * s_unit + s_lane;
+            if constexpr (SB == 2) sw[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + so));
+            else sw[k] = *reinterpret_cast<const uint32_t*>(sbase + so);
+        };
+        auto load_codes = [&](int k) {
+            const uint32_t co = uint32_t(min(u + k, ub - 1)) * c_unit + c_lane;
 #pragma unroll
             for (int p = 0; p < P; ++p)
                 cw[k][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + co + uint32_t(p) * c_part));
-            const uint32_t so = uu * s_unit + s_lane;
-            if constexpr (SB == 2) sw[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sbase + so));
-            else sw[k] = *reinterpret_cast<const uint32_t*>(sbase + so);
+        };
+        if constexpr (scales_first(FMT)) {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_scale(k);
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_codes(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                load_codes(k);
+                load_scale(k);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -345,14 +357,8 @@ __device__ __forceinline__ void q8_accumulate(const Q8ActArgs& a, const Q8Wave& 
         }
         __builtin_amdgcn_sched_barrier(0);
         Q8Unit<FMT> b[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
+        auto load_scale = [&](int k) {
             const uint32_t uu = uint32_t(min(u + k, L.ub - 1));
-            const uint32_t co = uu * L.c_unit + L.c_lane;
-#pragma unroll
-            for (int p = 0; p < P; ++p)
-                b[k].c[p] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
             const uint8_t* sp = L.sbase + uu * L.s_unit;
             if constexpr (FULL && SB == 2) {
                 const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sp + L.s_row[0]));
@@ -371,6 +377,26 @@ __device__ __forceinline__ void q8_accumulate(const Q8ActArgs& a, const Q8Wave& 
                         b[k].s[m] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp + L.s_row[m]));
                     else b[k].s[m] = *reinterpret_cast<const uint32_t*>(sp + L.s_row[m]);
                 }
+            }
+        };
+        auto load_codes = [&](int k) {
+            const uint32_t uu = uint32_t(min(u + k, L.ub - 1));
+            const uint32_t co = uu * L.c_unit + L.c_lane;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                b[k].c[p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(L.cbase + co + uint32_t(p) * L.c_part));
+        };
+        if constexpr (scales_first(FMT)) {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_scale(k);
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) load_codes(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                load_codes(k);
+                load_scale(k);
             }
         }
         // The copies into LDS were issued before the batch's code and scale

@@ -25,16 +25,29 @@ namespace lq {
 // count, bytes an unrelated call left in the workspace) counts as no
 // arrival yet: the workspace needs no clearing.  The last arrival clears
 // the word, so a captured graph, which replays one tag, finds it clear on
-// every replay.  The loop ends: a compare-and-swap fails only when another
-// arrival of the tile moved the word, at most S - 1 times.
+// every replay.
+//
+// The first arrival claims the word with one compare-and-swap (from zero,
+// or from whatever else it holds); every later one finds the tag there and
+// counts itself with one fetch-add: the word keeps this launch's tag until
+// the last arrival clears it, which cannot happen before this arrival.  So
+// an arrival costs at most two atomics however many slices meet (a
+// compare-and-swap retried until it wins costs O(S^2) atomics per tile when
+// the S slices arrive together).  The claim loop ends: only an arrival of
+// this launch moves a word away from a foreign value, and after it the word
+// holds the tag.
 __device__ __forceinline__ bool splitk_arrive(uint64_t* cnt, uint64_t tag, int S) {
     const uint64_t base = tag << 16;
     uint64_t cur = 0;   // the usual state of a word before its first arrival
-    uint64_t next = base + 1;
-    while (!__hip_atomic_compare_exchange_strong(cnt, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-        next = ((cur & ~uint64_t(0xFFFF)) == base) ? cur + 1 : base + 1;
-    const bool last = (next & 0xFFFF) == uint64_t(S);
+    uint64_t n = 1;
+    while (!__hip_atomic_compare_exchange_strong(cnt, &cur, base + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+        if ((cur & ~uint64_t(0xFFFF)) == base) {
+            n = (__hip_atomic_fetch_add(cnt, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) + 1;
+            break;
+        }
+    }
+    const bool last = n == uint64_t(S);
     if (last) __hip_atomic_store(cnt, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return last;
 }
