@@ -225,7 +225,7 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
             o.tiles = int32_t(tiles[i]);
             o.S = 1;
             o.wg0 = int32_t(wgs);
-            o.pad = 0;
+            o.tile_bytes = uint32_t(lq::kTileRows * nu[i] * lq::unit_bytes(fmt));
             o.part = nullptr;
             o.cnt = nullptr;
             wgs += tiles[i] * parts;
@@ -269,7 +269,7 @@ lq_status launch_chunk(int fmt, int xdt, int mt, const std::vector<GemvJob>& g, 
         o.tiles = int32_t(tiles[i]);
         o.S = int32_t(S[i]);
         o.wg0 = int32_t(wgs);
-        o.pad = 0;
+        o.tile_bytes = uint32_t(lq::kTileRows * nu[i] * lq::unit_bytes(fmt));
         o.part = nullptr;
         o.cnt = nullptr;
         if (S[i] > 1) {

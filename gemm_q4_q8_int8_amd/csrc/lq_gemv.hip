@@ -280,6 +280,13 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     const GemvDesc& D = a.d[find_matrix(a.wg0, bid)];
     const int N = D.N, nu = D.nu, S = D.S;
     const int local = bid - D.wg0;
+    // The fields the first loads need, all in one scalar round trip (the
+    // empty asm keeps the compiler from issuing the pointers' loads after
+    // the others have returned).
+    const uint8_t* const dcodes = D.codes;
+    const uint8_t* const dscales = D.scales;
+    const uint32_t dtb = D.tile_bytes;
+    asm volatile("" : : "s"(dcodes), "s"(dscales), "s"(dtb), "s"(N), "s"(nu), "s"(S), "s"(local));
     // Units [sa, sb) of this workgroup: slice `slice` of S.  (Unsplit
     // matrices skip the divisions: with a few units per wave they are a
     // noticeable share of the wave's scalar work.)
@@ -294,15 +301,18 @@ __global__ __launch_bounds__(64 * W) void gemv_kernel(const GemvArgs a) {
     const int nr = min(kTileRows, N - tile * kTileRows);
     const int rc = min(r, nr - 1);   // lanes past the last row re-read it and store nothing
 
-    // Units [ua, ub) of this wave: part w of W of the slice.
-    const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / W);
-    const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / W);
+    // Units [ua, ub) of this wave: part w of W of the slice (unsigned
+    // arithmetic: W is a power of two, so these are shifts).
+    const int ua = __builtin_amdgcn_readfirstlane(sa + int(uint32_t(sb - sa) * uint32_t(w) / W));
+    const int ub = __builtin_amdgcn_readfirstlane(sa + int(uint32_t(sb - sa) * uint32_t(w + 1) / W));
 
     // Uniform tile bases plus 32-bit per-lane offsets (scalar base + vector
-    // offset addressing).
-    const size_t first = size_t(tile) * kTileRows * size_t(nu);
-    const uint8_t* cbase = D.codes + first * UB;
-    const uint8_t* sbase = D.scales + first * SB;
+    // offset addressing).  A tile's scale bytes are its code bytes times
+    // SB / UB (1/8 or 1/16).
+    static_assert(UB % SB == 0 && ((UB / SB) & (UB / SB - 1)) == 0, "scale / code ratio");
+    const uint64_t tcode = uint64_t(uint32_t(tile)) * dtb;
+    const uint8_t* cbase = dcodes + tcode;
+    const uint8_t* sbase = dscales + tcode / (UB / SB);
     const uint32_t c_lane = uint32_t(rc) * 16u;
     const uint32_t c_unit = uint32_t(nr) * UB;
     const uint32_t c_part = uint32_t(nr) * 16u;

@@ -87,15 +87,32 @@ constexpr int64_t kMaxSlices = 4096;
 // Matrix of workgroup `bid` in a grouped launch.  wg0[i] is the first
 // workgroup of matrix i, INT32_MAX past the last matrix; the matrix is the
 // number of entries after the first that are not after bid.  The table
-// arrives in one scalar load and the count is branch-free scalar
-// arithmetic: a loop over the descriptors themselves made one dependent
-// scalar load per matrix before a wave's first weight load (0.6 us of the
-// 13.8 us Q8_0 decoder-layer launch).
+// arrives in one scalar load and the count is two scalar instructions per
+// entry (compare, add the carry).  A loop over the descriptors themselves
+// made one dependent scalar load per matrix before a wave's first weight
+// load (0.6 us of the 13.8 us Q8_0 decoder-layer launch), and every scalar
+// instruction before that load counts: the CU's one scalar unit serves all
+// its waves (64 more of them in the prologue cost that launch 0.25 us).
 template <int NB>
 __device__ inline int find_matrix(const int32_t (&wg0)[NB], int bid) {
     int di = 0;
+    if constexpr (NB == 16) {
+        // One block, so that no filler instructions separate the pairs.
+#define LQ_CMP_ADD(i) "s_cmp_ge_i32 %1, %" #i "\n\ts_addc_u32 %0, %0, 0\n\t"
+        asm(LQ_CMP_ADD(2) LQ_CMP_ADD(3) LQ_CMP_ADD(4) LQ_CMP_ADD(5) LQ_CMP_ADD(6) LQ_CMP_ADD(7) LQ_CMP_ADD(8)
+                LQ_CMP_ADD(9) LQ_CMP_ADD(10) LQ_CMP_ADD(11) LQ_CMP_ADD(12) LQ_CMP_ADD(13) LQ_CMP_ADD(14)
+                    LQ_CMP_ADD(15) LQ_CMP_ADD(16)
+            : "+s"(di)
+            : "s"(bid), "s"(wg0[1]), "s"(wg0[2]), "s"(wg0[3]), "s"(wg0[4]), "s"(wg0[5]), "s"(wg0[6]),
+              "s"(wg0[7]), "s"(wg0[8]), "s"(wg0[9]), "s"(wg0[10]), "s"(wg0[11]), "s"(wg0[12]), "s"(wg0[13]),
+              "s"(wg0[14]), "s"(wg0[15])
+            : "scc");
+#undef LQ_CMP_ADD
+    } else {
 #pragma unroll
-    for (int i = 1; i < NB; ++i) di += int(uint32_t(wg0[i] - 1 - bid) >> 31);
+        for (int i = 1; i < NB; ++i)
+            asm("s_cmp_ge_i32 %1, %2\n\ts_addc_u32 %0, %0, 0" : "+s"(di) : "s"(bid), "s"(wg0[i]) : "scc");
+    }
     return di;
 }
 template <int NB, class Desc>
@@ -201,7 +218,7 @@ struct GemvDesc {
     int32_t tiles;          // ceil(N / 64)
     int32_t S;              // K slices (workgroups per tile)
     int32_t wg0;            // first workgroup of this matrix in the launch
-    int32_t pad;
+    uint32_t tile_bytes;    // code bytes of one 64-row tile (64 * nu * unit_bytes)
 };
 
 struct GemvArgs {
