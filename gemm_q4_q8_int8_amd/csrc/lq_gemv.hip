@@ -85,10 +85,35 @@ __device__ __forceinline__ Q4Pairs q4_pairs(uint32_t d) {
     return p;
 }
 
+// The 32 fp32 activations of one unit, wave-uniform, as two 64-byte scalar
+// loads (x is 16-byte aligned; a scalar load needs only dword alignment, and
+// the type says no more).  Eight-dword loads with a wait per pair cost the
+// Q8_0 decoder layer 0.26 us (12.89 -> 12.63 us with these).
+typedef float f32x16v __attribute__((ext_vector_type(16), aligned(4)));
+typedef const __attribute__((address_space(4))) f32x16v* cf32x16_p;
+__device__ __forceinline__ void load_x32(cf32_p x, float (&o)[32]) {
+    const f32x16v a = *reinterpret_cast<cf32x16_p>(x), b = *reinterpret_cast<cf32x16_p>(x + 16);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        o[k] = a[k];
+        o[16 + k] = b[k];
+    }
+}
+// The same for 32 fp16 activations (16 dwords, one 64-byte load).
+typedef uint32_t u32x16v __attribute__((ext_vector_type(16), aligned(4)));
+typedef const __attribute__((address_space(4))) u32x16v* cu32x16_p;
+__device__ __forceinline__ void load_x16(cu32_p x, uint32_t (&o)[16]) {
+    const u32x16v a = *reinterpret_cast<cu32x16_p>(x);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o[k] = a[k];
+}
+
 // sum_e (q_e - 8) x_e over one Q4_0 block, fp32 activations in SGPRs.  The
 // high-nibble sum is 16x too large and is scaled by 1/16 (exact) at the end.
-__device__ __forceinline__ float dot_q4_0_f32(const u32x4 c, cf32_p x) {
+__device__ __forceinline__ float dot_q4_0_f32(const u32x4 c, cf32_p x0) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float x[32];
+    load_x32(x0, x);
     float s_lo = 0.0f, s_hi = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -126,13 +151,16 @@ __device__ __forceinline__ void dot_q4_0_f16(const u32x4 c, const cu32_p (&x)[MT
     float s_lo[MT], s_hi[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) s_lo[t] = s_hi[t] = 0.0f;
+    uint32_t xv[MT][16];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) load_x16(x[t], xv[t]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const Q4Pairs p = q4_pairs(w[i]);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const uint32_t a = x[t][2 * i], b = x[t][2 * i + 1];          // x 4i .. 4i+3
-            const uint32_t ah = x[t][8 + 2 * i], bh = x[t][8 + 2 * i + 1]; // x 16+4i .. 16+4i+3
+            const uint32_t a = xv[t][2 * i], b = xv[t][2 * i + 1];          // x 4i .. 4i+3
+            const uint32_t ah = xv[t][8 + 2 * i], bh = xv[t][8 + 2 * i + 1]; // x 16+4i .. 16+4i+3
             s_lo[t] = __builtin_amdgcn_fdot2(p.t0, pack_ll(a, b), s_lo[t], false);
             s_lo[t] = __builtin_amdgcn_fdot2(p.t2, pack_hh(a, b), s_lo[t], false);
             s_hi[t] = __builtin_amdgcn_fdot2(p.t1, pack_ll(ah, bh), s_hi[t], false);
@@ -162,8 +190,10 @@ LQ_SBYTE_TO_F32(sbyte3, "BYTE_3")
 
 // sum_e c_e x_e over 32 int8 codes (two 16-byte parts, element order), fp32
 // activations in SGPRs.
-__device__ __forceinline__ float dot_i8_f32(const u32x4 c0, const u32x4 c1, cf32_p x) {
+__device__ __forceinline__ float dot_i8_f32(const u32x4 c0, const u32x4 c1, cf32_p x0) {
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float x[32];
+    load_x32(x0, x);
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -186,8 +216,12 @@ __device__ __forceinline__ void dot_i8_f16(const u32x4 c0, const u32x4 c1, const
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
     float s0[MT], s1[MT];
+    uint32_t xv[MT][16];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) s0[t] = s1[t] = 0.0f;
+    for (int t = 0; t < MT; ++t) {
+        s0[t] = s1[t] = 0.0f;
+        load_x16(x[t] + xoff, xv[t]);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t u = w[i] ^ 0x80808080u;
@@ -195,8 +229,8 @@ __device__ __forceinline__ void dot_i8_f16(const u32x4 c0, const u32x4 c1, const
         const half2_t p23 = as_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            s0[t] = __builtin_amdgcn_fdot2(p01, as_half2(x[t][xoff + 2 * i]), s0[t], false);
-            s1[t] = __builtin_amdgcn_fdot2(p23, as_half2(x[t][xoff + 2 * i + 1]), s1[t], false);
+            s0[t] = __builtin_amdgcn_fdot2(p01, as_half2(xv[t][2 * i]), s0[t], false);
+            s1[t] = __builtin_amdgcn_fdot2(p23, as_half2(xv[t][2 * i + 1]), s1[t], false);
         }
     }
 #pragma unroll
