@@ -497,7 +497,15 @@ __global__ __launch_bounds__(1024) void gemv_sub_kernel(const GemvArgs a) {
     const GemvDesc& D = a.d[find_matrix(a.wg0, bid)];
     const int N = D.N, nu = D.nu;
     const int local = bid - D.wg0;
-    const int tile = local / P;
+    // Every descriptor field the first loads need, in one scalar round trip
+    // (as in gemv_kernel: these launches are small, so the prologue's
+    // latency is a large part of them).
+    const uint8_t* const dcodes = D.codes;
+    const uint8_t* const dscales = D.scales;
+    const void* const dx = D.x;
+    const uint32_t dtb = D.tile_bytes;
+    asm volatile("" : : "s"(dcodes), "s"(dscales), "s"(dx), "s"(dtb), "s"(N), "s"(nu), "s"(local));
+    const int tile = int(uint32_t(local) / P);
     const int sub = local - tile * P;
     const int nr = min(kTileRows, N - tile * kTileRows);
     if (sub * RPW >= nr) return;   // whole workgroup: past the last row of a ragged tile
@@ -506,12 +514,12 @@ __global__ __launch_bounds__(1024) void gemv_sub_kernel(const GemvArgs a) {
     const int p = l / RPW;
     const int rr = sub * RPW + (l - p * RPW);   // row within the tile
     const int rc = min(rr, nr - 1);              // rows past the last re-read it and store nothing
-    const int ua = __builtin_amdgcn_readfirstlane(nu * w / W);
-    const int ub = __builtin_amdgcn_readfirstlane(nu * (w + 1) / W);
+    const int ua = __builtin_amdgcn_readfirstlane(int(uint32_t(nu) * uint32_t(w) / W));
+    const int ub = __builtin_amdgcn_readfirstlane(int(uint32_t(nu) * uint32_t(w + 1) / W));
 
-    const size_t first = size_t(tile) * kTileRows * size_t(nu);
-    const uint8_t* cbase = D.codes + first * UB;
-    const uint8_t* sbase = D.scales + first * SB;
+    const uint64_t tcode = uint64_t(uint32_t(tile)) * dtb;   // tile base; scales: SB / UB of it
+    const uint8_t* cbase = dcodes + tcode;
+    const uint8_t* sbase = dscales + tcode / (UB / SB);
     const uint32_t c_lane = uint32_t(p) * uint32_t(nr) * 16u + uint32_t(rc) * 16u;
     const uint32_t c_unit = uint32_t(nr) * UB;
     const uint32_t s_lane = uint32_t(rc) * SB;
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(1024) void gemv_sub_kernel(const GemvArgs a) {
     constexpr int XV = XB;                     // 16-byte loads per 16 activations
     using XT = typename std::conditional<XDT == kF32, f32x4, u32x4>::type;
     const size_t xrow = size_t(nu) * E * XB / 16;   // one token's activations, in 16-byte units
-    const XT* xb = reinterpret_cast<const XT*>(static_cast<const uint8_t*>(D.x) + size_t(p) * 16 * XB);
+    const XT* xb = reinterpret_cast<const XT*>(static_cast<const uint8_t*>(dx) + size_t(p) * 16 * XB);
 
     float acc[MT];
 #pragma unroll

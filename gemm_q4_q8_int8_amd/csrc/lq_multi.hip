@@ -265,8 +265,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
 
     const int bid = int(blockIdx.x);
     const MultiDesc& D = a.d[find_matrix(a.wg0, bid)];
-    const int N = D.N, nu = D.nu, S = D.S, M = D.M;
+    const int N = D.N, nu = D.nu, S = D.S, M = D.M, K = D.K;
     const int local = bid - D.wg0;
+    // Every descriptor field the first loads need, in one scalar round trip
+    // (the empty asm keeps the compiler from fetching the pointers after the
+    // integers have returned).
+    const uint8_t* const dcodes = D.codes;
+    const uint8_t* const dscales = D.scales;
+    const _Float16* const dx = D.x;
+    const int tiles = D.tiles;
+    asm volatile("" : : "s"(dcodes), "s"(dscales), "s"(dx), "s"(N), "s"(nu), "s"(S), "s"(M), "s"(K), "s"(tiles),
+                 "s"(local));
     const int tile = int(uint32_t(local) / uint32_t(S));
     const int slice = local - tile * S;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
@@ -277,13 +286,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
 
     int sa, sb;
     slice_units(nu, S, slice, sa, sb);
-    const int ua = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * w / 4);
-    const int ub = __builtin_amdgcn_readfirstlane(sa + (sb - sa) * (w + 1) / 4);
+    const int ua = __builtin_amdgcn_readfirstlane(sa + int(uint32_t(sb - sa) * uint32_t(w) / 4));
+    const int ub = __builtin_amdgcn_readfirstlane(sa + int(uint32_t(sb - sa) * uint32_t(w + 1) / 4));
 
     const size_t first = size_t(tile) * kTileRows * size_t(nu);
     WaveLoop L;
-    L.cbase = D.codes + first * UB;
-    L.sbase = D.scales + first * SB;
+    L.cbase = dcodes + first * UB;
+    L.sbase = dscales + first * SB;
     // Rows past the end of a partial tile are re-read from the last row and
     // never stored; so are tokens past M.
     L.c_lane = uint32_t(min(4 * r + g, nr - 1)) * 16u;
@@ -294,12 +303,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     for (int m = 0; m < 4; ++m) L.s_row[m] = uint32_t(min(4 * r + m, nr - 1)) * SB;
     // Q4_0 lane group g takes elements 4g..4g+3 and 16+4g.. of a block (the
     // nibbles of code dword g); int8 lane group g takes elements 8g..8g+7.
-    L.xrow = D.x + size_t(min(r, M - 1)) * size_t(D.K) + 8 * g;
-    L.xg = reinterpret_cast<const uint8_t*>(D.x);
+    L.xrow = dx + size_t(min(r, M - 1)) * size_t(K) + 8 * g;
+    L.xg = reinterpret_cast<const uint8_t*>(dx);
     L.xs = smem + w * XStage<FMT, UNR>::kBytes;
     L.x_row = uint32_t(min(r, M - 1)) * uint32_t(XStage<FMT, UNR>::P16) * 16u;
     L.M = M;
-    L.K = D.K;
+    L.K = K;
     L.ua = ua;
     L.ub = ub;
 
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_multi_kernel(const MultiArg
     }
     // Split K: publish this slice, then the last workgroup to arrive adds the
     // slices in slice order (lq_splitk.h).
-    const size_t pitch = size_t(D.tiles) * kTileRows;   // floats per token of one slice
+    const size_t pitch = size_t(tiles) * kTileRows;   // floats per token of one slice
     const size_t spitch = pitch * size_t(M);             // floats per slice
     if (token < M) {
         float* pp = D.part + size_t(slice) * spitch + size_t(token) * pitch + row0;
