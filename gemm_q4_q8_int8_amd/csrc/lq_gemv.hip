@@ -85,6 +85,29 @@ __device__ __forceinline__ Q4Pairs q4_pairs(uint32_t d) {
     return p;
 }
 
+// The same four pairs in element order, for fp16 activations: a byte permute
+// puts bytes (4i, 4i+1) and (4i+2, 4i+3) of the dword under 0x64, and one
+// mask per pair keeps the low or the high nibble:
+//   t0 = elements (4i, 4i+1), t2 = (4i+2, 4i+3),
+//   t1 = 16 x elements (16+4i, 16+4i+1), t3 = 16 x (16+4i+2, 16+4i+3).
+// One more vector instruction per dword than q4_pairs, but each pair then
+// meets an activation dword as loaded: the pairs q4_pairs gives needed four
+// scalar packs per dword and token, and the scalar unit (one per CU) was the
+// limit of the fp16 launches (two-token LM head: 371 scalar instructions
+// per wave).
+__device__ __forceinline__ Q4Pairs q4_pairs_seq(uint32_t d) {
+    const half2_t lo_off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2_t hi_off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t a = __builtin_amdgcn_perm(0x64646464u, d, 0x04010400u);   // [b0, 64, b1, 64]
+    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, d, 0x04030402u);   // [b2, 64, b3, 64]
+    Q4Pairs p;
+    p.t0 = as_half2(a & 0x640F640Fu) - lo_off;
+    p.t1 = as_half2(a & 0x64F064F0u) - hi_off;
+    p.t2 = as_half2(b & 0x640F640Fu) - lo_off;
+    p.t3 = as_half2(b & 0x64F064F0u) - hi_off;
+    return p;
+}
+
 // The 32 fp32 activations of one unit, wave-uniform, as two 64-byte scalar
 // loads (x is 16-byte aligned; a scalar load needs only dword alignment, and
 // the type says no more).  Eight-dword loads with a wait per pair cost the
@@ -130,19 +153,6 @@ __device__ __forceinline__ float dot_q4_0_f32(const u32x4 c, cf32_p x0) {
     return __builtin_fmaf(s_hi, 0.0625f, s_lo);
 }
 
-// Two fp16 values a.lo, b.lo (ll) or a.hi, b.hi (hh) as one pair.  The
-// activations are wave-uniform and sit in SGPRs: written as a shuffle this is
-// one scalar pack (the shift-and-or form became three scalar ops, and with
-// two tokens the scalar unit, shared by the CU's four SIMDs, was the limit).
-__device__ __forceinline__ half2_t pack_ll(uint32_t a, uint32_t b) {
-    return __builtin_shufflevector(as_half2(a), as_half2(b), 0, 2);
-}
-__device__ __forceinline__ half2_t pack_hh(uint32_t a, uint32_t b) {
-    uint32_t r;
-    asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(r) : "s"(a), "s"(b));
-    return as_half2(r);
-}
-
 // Same sum with fp16 activations for MT tokens: x[t] holds token t's pairs
 // (x_2i, x_2i+1).  The nibbles are unpacked once for all tokens.
 template <int MT>
@@ -156,15 +166,13 @@ __device__ __forceinline__ void dot_q4_0_f16(const u32x4 c, const cu32_p (&x)[MT
     for (int t = 0; t < MT; ++t) load_x16(x[t], xv[t]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const Q4Pairs p = q4_pairs(w[i]);
+        const Q4Pairs p = q4_pairs_seq(w[i]);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const uint32_t a = xv[t][2 * i], b = xv[t][2 * i + 1];          // x 4i .. 4i+3
-            const uint32_t ah = xv[t][8 + 2 * i], bh = xv[t][8 + 2 * i + 1]; // x 16+4i .. 16+4i+3
-            s_lo[t] = __builtin_amdgcn_fdot2(p.t0, pack_ll(a, b), s_lo[t], false);
-            s_lo[t] = __builtin_amdgcn_fdot2(p.t2, pack_hh(a, b), s_lo[t], false);
-            s_hi[t] = __builtin_amdgcn_fdot2(p.t1, pack_ll(ah, bh), s_hi[t], false);
-            s_hi[t] = __builtin_amdgcn_fdot2(p.t3, pack_hh(ah, bh), s_hi[t], false);
+            s_lo[t] = __builtin_amdgcn_fdot2(p.t0, as_half2(xv[t][2 * i]), s_lo[t], false);          // x 4i, 4i+1
+            s_lo[t] = __builtin_amdgcn_fdot2(p.t2, as_half2(xv[t][2 * i + 1]), s_lo[t], false);      // x 4i+2, 4i+3
+            s_hi[t] = __builtin_amdgcn_fdot2(p.t1, as_half2(xv[t][8 + 2 * i]), s_hi[t], false);      // x 16+4i ..
+            s_hi[t] = __builtin_amdgcn_fdot2(p.t3, as_half2(xv[t][8 + 2 * i + 1]), s_hi[t], false);
         }
     }
 #pragma unroll
