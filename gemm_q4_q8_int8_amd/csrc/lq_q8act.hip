@@ -78,6 +78,39 @@ __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(const void* _
     sum[b] = t;
 }
 
+// N consecutive wave-uniform dwords (N = 1, 2, 4, 8 or a multiple of 16) as
+// the widest scalar loads (dword alignment is all a scalar load needs).
+template <int N>
+__device__ __forceinline__ void sload(ci32_p p, int32_t (&o)[N]) {
+    typedef int32_t v16 __attribute__((ext_vector_type(16), aligned(4)));
+    typedef int32_t v8 __attribute__((ext_vector_type(8), aligned(4)));
+    typedef int32_t v4 __attribute__((ext_vector_type(4), aligned(4)));
+    typedef int32_t v2 __attribute__((ext_vector_type(2), aligned(4)));
+    if constexpr (N % 16 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 16; ++i) {
+            const v16 v = *reinterpret_cast<const __attribute__((address_space(4))) v16*>(p + 16 * i);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) o[16 * i + k] = v[k];
+        }
+    } else if constexpr (N == 8) {
+        const v8 v = *reinterpret_cast<const __attribute__((address_space(4))) v8*>(p);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = v[k];
+    } else if constexpr (N == 4) {
+        const v4 v = *reinterpret_cast<const __attribute__((address_space(4))) v4*>(p);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = v[k];
+    } else if constexpr (N == 2) {
+        const v2 v = *reinterpret_cast<const __attribute__((address_space(4))) v2*>(p);
+        o[0] = v[0];
+        o[1] = v[1];
+    } else {
+        static_assert(N == 1, "dword count");
+        o[0] = p[0];
+    }
+}
+
 // Integer dot product of one block, added to I: code dwords c[0..7] (signed
 // bytes; for Q4_0 the nibbles of the 4 code dwords, below) with activation
 // dwords x[0..7].
@@ -156,6 +189,57 @@ __global__ __launch_bounds__(64 * W) void gemv_q8act_kernel(const Q8ActArgs a) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        // Q4_0: code dword i's low nibbles are elements 4i .. 4i + 3 of the
+        // block, its high nibbles 16 + 4i .., both as the stored values q + 8
+        // (0 .. 15); the int8 formats: code part 2 xb + h holds elements
+        // 16 h .. 16 h + 15 of the unit's block xb.
+        auto codes_of = [&](int k, int xb, uint32_t (&c)[8]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (FMT == kQ4_0) {
+                    c[i] = cw[k][0][i] & 0x0F0F0F0Fu;
+                    c[4 + i] = (cw[k][0][i] >> 4) & 0x0F0F0F0Fu;
+                } else {
+                    c[i] = cw[k][2 * xb][i];
+                    c[4 + i] = cw[k][2 * xb + 1][i];
+                }
+            }
+        };
+        if (u + UNR <= ub) {
+            // A whole batch: each token's activation codes, scales and code
+            // sums of the batch's UNR * XB consecutive blocks in a few wide
+            // scalar loads (one load of each per block and token made this
+            // kernel bound by the CU's scalar unit: 402 scalar instructions
+            // per wave at four tokens).
+            constexpr int NB = UNR * XB;
+            uint32_t c[NB][8];
+#pragma unroll
+            for (int k = 0; k < UNR; ++k)
+#pragma unroll
+                for (int xb = 0; xb < XB; ++xb) codes_of(k, xb, c[k * XB + xb]);
+            float ws[UNR];
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                if constexpr (fp32_scale(FMT)) ws[k] = __uint_as_float(sw[k]);
+                else ws[k] = (float)__builtin_bit_cast(_Float16, uint16_t(sw[k]));
+            }
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const size_t b0 = size_t(t) * size_t(nb) + size_t(u) * XB;
+                int32_t xq[NB * 8], xs[NB], xsum[NB];
+                sload<NB * 8>((ci32_p)(a.q) + b0 * 8, xq);
+                sload<NB>((ci32_p)(a.s) + b0, xs);
+                if constexpr (FMT == kQ4_0) sload<NB>((ci32_p)(a.sum) + b0, xsum);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    int I = FMT == kQ4_0 ? -8 * xsum[b] : 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) I = __builtin_amdgcn_sdot4(int(c[b][i]), xq[8 * b + i], I, false);
+                    acc[t] = __builtin_fmaf(ws[b / XB] * __int_as_float(xs[b]), float(I), acc[t]);
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
             if (u + k >= ub) break;   // uniform
